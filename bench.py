@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""MoE-layer benchmark on one MI355X.
+
+A step is one moe_chunked_forward call: routing metadata for every chunk,
+then per chunk permute -> gate/up GEMM + SwiGLU -> down GEMM -> weighted
+combine, chunks paired on two HIP streams.  Inputs are seeded synthetic data
+already resident in HBM when the timed region starts.
+
+Prints ONE JSON line: MoE-layer tokens/s (T / seconds per step), the roofline
+of the dominant kernel (the gate/up grouped GEMM) measured live with HIP
+events on the stream it runs on, and the CPU oracle timed on the host cores on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--num-chunks N]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s (permute+expert GEMM+combine); % HBM / % MFMA peak"
+HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense FLOP/s (fp32: matrix/vector peak)
+GATE_UP_SRC = os.path.join(ROOT, "combine_top_route_expert_amd", "csrc", "gemm_bf16.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def make_inputs(cfg, torch, synth):
+    import numpy as np
+    idx, w = synth.routing(cfg)
+    hidden = synth.hidden_states(cfg, "cuda")
+    wgu, wd = synth.all_expert_weights(cfg, "cuda")
+    torch.cuda.synchronize()
+    return {"hidden": hidden, "idx": torch.from_numpy(idx).cuda(),
+            "w": torch.from_numpy(w).cuda(), "wgu": wgu, "wd": wd,
+            "idx_np": idx, "w_np": w, "counts": np.bincount(idx.ravel(), minlength=cfg.E)}
+
+
+def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True):
+    cfg_dtype = shape.torch_dtype
+    out = torch.empty((shape.T, shape.H), dtype=cfg_dtype, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else None
+
+    def step():
+        moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"],
+                                inp["wd"], out, ws, err, s0=s0, s1=s1)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s0)
+    for _ in range(steps):
+        step()
+    e1.record(s0)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"wall_ms": wall_ms, "event_ms": e0.elapsed_time(e1) / steps,
+            "workspace_bytes": ws.numel(), "dev_error": int(err.item())}
+
+
+def kernel_times(moe, torch, shape, inp, reps):
+    """Average duration of each step's launch on chunk 0, HIP events on the
+    stream the kernels run on (torch's current stream)."""
+    T, k, E, N, G, H, I = shape.T, shape.k, shape.E, shape.N, shape.G, shape.H, shape.I
+    dt = shape.torch_dtype
+    i32 = dict(dtype=torch.int32, device="cuda")
+    counts = torch.empty((N, E), **i32)
+    offsets = torch.empty((N, E + 1), **i32)
+    splits = torch.empty((N, G), **i32)
+    src_row = torch.empty(T * k, **i32)
+    dst_row = torch.empty(T * k, **i32)
+    err = torch.empty(1, **i32)
+    mws = torch.empty(moe.moe_route_meta_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    t0, t1 = moe.moe_chunk_range(shape, 0)
+    rows = (t1 - t0) * k
+    xp = torch.empty((rows, H), dtype=dt, device="cuda")
+    act = torch.empty((rows, I), dtype=dt, device="cuda")
+    y = torch.empty((rows, H), dtype=dt, device="cuda")
+    out = torch.empty((T, H), dtype=dt, device="cuda")
+    s = torch.cuda.current_stream()
+    calls = {
+        "route_meta": lambda: moe.moe_route_meta(shape, inp["idx"], counts, offsets, splits,
+                                                 src_row, dst_row, err, mws, s),
+        "permute": lambda: moe.moe_permute(shape, 0, inp["hidden"], dst_row, xp, s),
+        "gate_up": lambda: moe.moe_expert_gate_up(shape, 0, xp, offsets, inp["wgu"], act, s),
+        "down": lambda: moe.moe_expert_down(shape, 0, act, offsets, inp["wd"], y, s),
+        "combine": lambda: moe.moe_unpermute_combine(shape, 0, y, dst_row, inp["w"], out, s),
+    }
+    res = {}
+    for name, fn in calls.items():
+        fn()
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / reps  # microseconds per launch
+    c0 = counts[0].cpu()
+    return res, int(c0.sum().item()), int((c0 > 0).sum().item()), rows
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
+
+
+def load_traffic(config_name, N):
+    """HBM bytes per gate/up launch from committed rocprofv3 --pmc counters, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"gate_up_gemm_{config_name}_N{N}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != source_sha(GATE_UP_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, synth, target_s=15.0):
+    """The oracle, as it stands, on a bounded prefix of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    hid = synth.to_f64(inp["hidden"])
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = (synth.to_f64(inp["wgu"][e]), synth.to_f64(inp["wd"][e]))
+        return cache[e]
+
+    def run(ts):
+        for e in np.unique(inp["idx_np"][:ts]):
+            get(int(e))  # input conversion happens outside the timed region
+        t = time.perf_counter()
+        oracle.moe_forward(hid[:ts], inp["idx_np"][:ts], inp["w_np"][:ts], get, cfg.E, cfg.I,
+                           cfg.groups, 1)
+        return time.perf_counter() - t
+
+    ts = min(cfg.T, 128)
+    el = run(ts)
+    while el < target_s / 3 and ts < cfg.T:
+        ts = min(cfg.T, max(ts * 2, int(ts * target_s / max(el, 1e-3))))
+        el = run(ts)
+    return {"value": ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {ts} of {cfg.T} tokens of {cfg.name} (N=1), float64 numpy oracle, "
+                      f"{el:.1f} s; expert weights converted to float64 outside the timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="bf16_e64_zipf")
+    ap.add_argument("--num-chunks", type=int, default=2)
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this MoE layer build runs on one "
+              "GPU only (no multi-GPU path); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_top_route_expert_amd as moe
+    import synth
+
+    moe.load_library()
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    N = args.num_chunks
+    log(f"inputs {cfg.name}")
+    inp = make_inputs(cfg, torch, synth)
+    shape = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, N, cfg.dtype)
+
+    log(f"layer N={N}")
+    main_run = time_layer(moe, torch, shape, inp, args.steps, args.warmup)
+    log(f"layer N=1 (reference)")
+    shape1 = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, 1, cfg.dtype)
+    run1 = time_layer(moe, torch, shape1, inp, args.steps, args.warmup, two_streams=False)
+    log("per-kernel timing")
+    kt, rows0, e_act0, _ = kernel_times(moe, torch, shape, inp, args.kernel_reps)
+    copy_bw = copy_bandwidth(torch)
+
+    s = cfg.elem_bytes
+    H, I = cfg.H, cfg.I
+    gu_bytes = rows0 * H * s + e_act0 * 2 * I * H * s + rows0 * I * s
+    gu_flops = 2.0 * rows0 * H * 2 * I
+    gu_s = kt["gate_up"] * 1e-6
+    peak_f = MFMA_PEAK[cfg.dtype]
+    if gu_bytes / HBM_PEAK >= gu_flops / peak_f:
+        roof = {"bound": "hbm", "achieved": gu_bytes / gu_s / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_f / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    traffic = load_traffic(cfg.name, N)
+    roof["traffic"] = traffic
+    roof["kernel"] = "grouped_gemm_bf16<gate_up> (moe_expert_gate_up), chunk 0"
+    roof["algorithmic_bytes_per_launch"] = gu_bytes
+    roof["algorithmic_flop_per_launch"] = gu_flops
+    roof["avg_launch_us"] = kt["gate_up"]
+    roof["mfma_frac"] = gu_flops / gu_s / peak_f
+
+    ms = main_run["wall_ms"]
+    line = {
+        "metric": METRIC, "value": cfg.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": H, "E": cfg.E, "top_k": cfg.k,
+                   "I": I, "num_chunks": N, "streams": 2, "groups": cfg.groups},
+        "roofline": roof,
+        "kernels_us_chunk0": kt,
+        "event_ms_per_step": main_run["event_ms"],
+        "unchunked": {"ms_per_step": run1["wall_ms"], "value": cfg.T / (run1["wall_ms"] * 1e-3)},
+        "workspace_bytes": {"N": main_run["workspace_bytes"], "N1": run1["workspace_bytes"]},
+        "copy_bandwidth_GBps": copy_bw / 1e9,
+        "expert_load": {"max_over_mean": float(inp["counts"].max() / inp["counts"].mean()),
+                        "empty_experts": int((inp["counts"] == 0).sum())},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, synth)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+// Routing metadata for every chunk in one pass: per-expert counts, exclusive
+// offsets, destination-group send splits and the stable permutation
+// (src_row / dst_row).
+//
+// MindSpeed Chunk MoE article, timing-diagram section: the metadata of all
+// chunks is produced once, not per chunk.  MindSpore news page, "# 02
+// AlltoAllV收发异构复用特性": the send lists stay on the device and combine
+// reuses dispatch's lists (here dst_row), so nothing is copied to the host.
+//
+// Three launches, all atomics-free and deterministic:
+//  1. meta_hist : one wave per segment of kMetaSeg assignments (segments never
+//     straddle a chunk).  Lanes with equal expert id find each other with one
+//     ballot per id bit; the lowest such lane adds the group's popcount to the
+//     wave's LDS counter.  Writes seg_counts[seg][E] and the dropped-id count.
+//  2. meta_scan : one workgroup.  Per chunk and expert, an exclusive prefix over
+//     the chunk's segments (in place), then a block-wide exclusive scan over
+//     experts gives offsets; seg_counts becomes each segment's first row per
+//     expert.  Also counts, group splits, the -1 tail of src_row and dev_error.
+//  3. meta_rank : one wave per segment again.  rank = popcount(peers below me)
+//     plus the segment's running base per expert gives dst_row[f] and
+//     src_row[chunk_start + row] = f.  Lanes are walked in ascending f, so the
+//     permutation is stable.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+struct MetaArgs {
+  const int32_t* idx;
+  int32_t* seg_counts;
+  int32_t* seg_invalid;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* splits;
+  int32_t* src_row;
+  int32_t* dst_row;
+  int32_t* dev_error;
+  int T, k, E, G, N, Tc, spc, id_bits;
+};
+
+// Segment `seg` -> its chunk and flat range [f_lo, f_hi).
+__device__ __forceinline__ void seg_range(const MetaArgs& a, int seg, int* chunk, int* f_lo,
+                                          int* f_hi, int* chunk_f0) {
+  int c = seg / a.spc, j = seg - c * a.spc;
+  long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
+  if (t0 > a.T) t0 = a.T;
+  if (t1 > a.T) t1 = a.T;
+  long long lo = t0 * a.k + (long long)j * kMetaSeg;
+  long long hi = lo + kMetaSeg;
+  if (hi > t1 * a.k) hi = t1 * a.k;
+  if (lo > hi) lo = hi;
+  *chunk = c;
+  *f_lo = (int)lo;
+  *f_hi = (int)hi;
+  *chunk_f0 = (int)(t0 * a.k);
+}
+
+// Mask of the lanes whose (valid) expert id equals this lane's.
+__device__ __forceinline__ uint64_t peer_mask(int e, bool ok, int id_bits) {
+  uint64_t m = __ballot(ok);
+  for (int b = 0; b < id_bits; ++b) {
+    bool bit = (e >> b) & 1;
+    uint64_t vb = __ballot(bit);
+    m &= bit ? vb : ~vb;
+  }
+  return m;
+}
+
+__global__ void __launch_bounds__(64) meta_hist(MetaArgs a) {
+  extern __shared__ int cnt[];
+  const int lane = threadIdx.x;
+  int c, f_lo, f_hi, cf0;
+  seg_range(a, blockIdx.x, &c, &f_lo, &f_hi, &cf0);
+  for (int e = lane; e < a.E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  int invalid = 0;
+  for (int base = f_lo; base < f_hi; base += 64) {
+    int f = base + lane;
+    bool active = f < f_hi;
+    int e = active ? a.idx[f] : -1;
+    bool ok = active && e >= 0 && e < a.E;
+    invalid += (active && !ok) ? 1 : 0;
+    uint64_t peers = peer_mask(e, ok, a.id_bits);
+    if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) cnt[e] += __popcll(peers);
+    __syncthreads();
+  }
+  int32_t* out = a.seg_counts + (size_t)blockIdx.x * a.E;
+  for (int e = lane; e < a.E; e += 64) out[e] = cnt[e];
+  for (int d = 32; d > 0; d >>= 1) invalid += __shfl_xor(invalid, d);
+  if (lane == 0) a.seg_invalid[blockIdx.x] = invalid;
+}
+
+// Exclusive block scan of one value per thread (blockDim.x == 1024).
+__device__ int block_exclusive_scan(int v, int* total, int* lds_waves) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    int n = __shfl_up(incl, d);
+    if (lane >= d) incl += n;
+  }
+  if (lane == 63) lds_waves[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? lds_waves[lane] : 0;
+    int wi = w;
+    for (int d = 1; d < 16; d <<= 1) {
+      int n = __shfl_up(wi, d);
+      if (lane >= d) wi += n;
+    }
+    if (lane < 16) lds_waves[16 + lane] = wi - w;  // exclusive wave prefix
+    if (lane == 15) lds_waves[32] = wi;
+  }
+  __syncthreads();
+  int r = incl - v + lds_waves[16 + wave];
+  *total = lds_waves[32];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
+  __shared__ int lds_waves[48];
+  __shared__ int off_lds[1025];
+  const int e = threadIdx.x;
+  const bool has_e = e < a.E;
+  for (int c = 0; c < a.N; ++c) {
+    const size_t seg0 = (size_t)c * a.spc;
+    int run = 0;
+    if (has_e) {
+      for (int j = 0; j < a.spc; ++j) {
+        int32_t* p = a.seg_counts + (seg0 + j) * a.E + e;
+        int v = *p;
+        *p = run;
+        run += v;
+      }
+    }
+    int total;
+    int off = block_exclusive_scan(has_e ? run : 0, &total, lds_waves);
+    if (has_e) {
+      a.counts[(size_t)c * a.E + e] = run;
+      a.offsets[(size_t)c * (a.E + 1) + e] = off;
+      off_lds[e] = off;
+      for (int j = 0; j < a.spc; ++j) a.seg_counts[(seg0 + j) * a.E + e] += off;
+    }
+    if (e == 0) {
+      a.offsets[(size_t)c * (a.E + 1) + a.E] = total;
+      off_lds[a.E] = total;
+    }
+    __syncthreads();
+    const int per = a.E / a.G;
+    for (int g = threadIdx.x; g < a.G; g += blockDim.x)
+      a.splits[(size_t)c * a.G + g] = off_lds[(g + 1) * per] - off_lds[g * per];
+    // rows past the chunk's valid rows hold no assignment
+    long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
+    if (t0 > a.T) t0 = a.T;
+    if (t1 > a.T) t1 = a.T;
+    const long long f0 = t0 * a.k, ac = (t1 - t0) * a.k;
+    for (long long r = total + threadIdx.x; r < ac; r += blockDim.x) a.src_row[f0 + r] = -1;
+    __syncthreads();
+  }
+  if (a.dev_error) {
+    int s = 0;
+    const long long nseg = (long long)a.N * a.spc;
+    for (long long i = threadIdx.x; i < nseg; i += blockDim.x) s += a.seg_invalid[i];
+    int total;
+    (void)block_exclusive_scan(s, &total, lds_waves);
+    if (threadIdx.x == 0) *a.dev_error = total;
+  }
+}
+
+__global__ void __launch_bounds__(64) meta_rank(MetaArgs a) {
+  extern __shared__ int base[];
+  const int lane = threadIdx.x;
+  int c, f_lo, f_hi, cf0;
+  seg_range(a, blockIdx.x, &c, &f_lo, &f_hi, &cf0);
+  (void)c;
+  const int32_t* sb = a.seg_counts + (size_t)blockIdx.x * a.E;
+  for (int e = lane; e < a.E; e += 64) base[e] = sb[e];
+  __syncthreads();
+  const uint64_t lt = lanemask_lt();
+  for (int b0 = f_lo; b0 < f_hi; b0 += 64) {
+    int f = b0 + lane;
+    bool active = f < f_hi;
+    int e = active ? a.idx[f] : -1;
+    bool ok = active && e >= 0 && e < a.E;
+    uint64_t peers = peer_mask(e, ok, a.id_bits);
+    int row = -1;
+    if (ok) row = base[e] + __popcll(peers & lt);
+    __syncthreads();  // every lane has read base[] before the leaders advance it
+    if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) base[e] += __popcll(peers);
+    if (active) a.dst_row[f] = row;
+    if (ok) a.src_row[cf0 + row] = f;
+    __syncthreads();
+  }
+}
+
+int bits_for(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+}  // namespace
+
+MetaPlan meta_plan(const Shape& s) {
+  MetaPlan p{};
+  int64_t ac = (int64_t)s.Tc * s.k;
+  p.segs_per_chunk = (int)((ac + kMetaSeg - 1) / kMetaSeg);
+  if (p.segs_per_chunk < 1) p.segs_per_chunk = 1;
+  p.nseg = (int64_t)s.N * p.segs_per_chunk;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  p.seg_counts_off = 0;
+  p.seg_invalid_off = al((size_t)p.nseg * s.E * sizeof(int32_t));
+  p.bytes = p.seg_invalid_off + al((size_t)p.nseg * sizeof(int32_t));
+  return p;
+}
+
+hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts,
+                             int32_t* offsets, int32_t* splits, int32_t* src_row,
+                             int32_t* dst_row, int32_t* dev_error, void* ws, hipStream_t st) {
+  MetaPlan p = meta_plan(s);
+  MetaArgs a{};
+  a.idx = idx;
+  a.seg_counts = (int32_t*)((char*)ws + p.seg_counts_off);
+  a.seg_invalid = (int32_t*)((char*)ws + p.seg_invalid_off);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.splits = splits;
+  a.src_row = src_row;
+  a.dst_row = dst_row;
+  a.dev_error = dev_error;
+  a.T = s.T;
+  a.k = s.k;
+  a.E = s.E;
+  a.G = s.G;
+  a.N = s.N;
+  a.Tc = s.Tc;
+  a.spc = p.segs_per_chunk;
+  a.id_bits = bits_for(s.E);
+  const size_t lds = (size_t)s.E * sizeof(int);
+  hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
+  hipLaunchKernelGGL(meta_scan, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

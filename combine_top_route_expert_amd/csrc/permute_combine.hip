@@ -1,0 +1,159 @@
+// Permute (dispatch side) and unpermute + weighted combine.
+//
+// MindSpeed Chunk MoE article, core principle and timing-diagram section:
+// tokens are permuted into an expert-contiguous buffer before the expert
+// computation and unpermuted back to token order after it, the latter weighted
+// by top_k_weights.  The combine reads the dispatch-side dst_row again rather
+// than recomputing any routing (MindSpore news page, "# 02": combine reuses
+// dispatch's lists).
+//
+// Both kernels are token-major: one wave owns one token row.
+//  * permute reads the token's row once (16-byte vectors, several in flight per
+//    lane) and writes it to each of its k destination rows; every destination
+//    row is written by exactly one wave, so no atomics are needed.
+//  * combine reads the token's k expert-output rows, accumulates
+//    w[t,j] * y[row_j] in fp32 in ascending j, and rounds once on the store.
+// Both are HBM-bound: permute moves T*H*s + A*H*s bytes, combine A*H*s + T*H*s.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kVecPerLane = 4;  // 16-byte vectors each lane keeps in flight per pass
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+permute_rows(const u32x4* __restrict__ hidden, const int32_t* __restrict__ dst_row,
+             u32x4* __restrict__ x_perm, int t0, int t1, int k, int nvec) {
+  const int lane = threadIdx.x & 63;
+  const int t = t0 + blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const u32x4* src = hidden + (size_t)t * nvec;
+  const int32_t* dr = dst_row + (size_t)t * k;
+  for (int v0 = 0; v0 < nvec; v0 += 64 * kVecPerLane) {
+    u32x4 buf[kVecPerLane];
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i) {
+      int v = v0 + i * 64 + lane;
+      if (v < nvec) buf[i] = src[v];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int r = dr[j];
+      if (r < 0) continue;
+      u32x4* dst = x_perm + (size_t)r * nvec;
+#pragma unroll
+      for (int i = 0; i < kVecPerLane; ++i) {
+        int v = v0 + i * 64 + lane;
+        if (v < nvec) dst[v] = buf[i];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& q, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(q[i] << 16);
+    f[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
+  u32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __bf16 lo = (__bf16)f[2 * i], hi = (__bf16)f[2 * i + 1];
+    q[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return q;
+}
+
+// One wave per token; each lane holds kVecPerLane 16-byte vectors of the row.
+template <bool kBf16>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+combine_rows(const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
+             const float* __restrict__ w, u32x4* __restrict__ out, int t0, int t1, int k,
+             int nvec) {
+  constexpr int kEl = kBf16 ? 8 : 4;  // elements per 16-byte vector
+  const int lane = threadIdx.x & 63;
+  const int t = t0 + blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int32_t* dr = dst_row + (size_t)t * k;
+  const float* wt = w + (size_t)t * k;
+  for (int v0 = 0; v0 < nvec; v0 += 64 * kVecPerLane) {
+    float acc[kVecPerLane][kEl];
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i)
+#pragma unroll
+      for (int q = 0; q < kEl; ++q) acc[i][q] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int r = dr[j];
+      if (r < 0) continue;
+      const float wj = wt[j];
+      const u32x4* src = y + (size_t)r * nvec;
+#pragma unroll
+      for (int i = 0; i < kVecPerLane; ++i) {
+        int v = v0 + i * 64 + lane;
+        if (v < nvec) {
+          u32x4 q = src[v];
+          float f[kEl];
+          if constexpr (kBf16) {
+            unpack_bf16x8(q, f);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(q[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < kEl; ++e) acc[i][e] = __builtin_fmaf(wj, f[e], acc[i][e]);
+        }
+      }
+    }
+    u32x4* dst = out + (size_t)t * nvec;
+#pragma unroll
+    for (int i = 0; i < kVecPerLane; ++i) {
+      int v = v0 + i * 64 + lane;
+      if (v < nvec) {
+        if constexpr (kBf16) {
+          dst[v] = pack_bf16x8(acc[i]);
+        } else {
+          u32x4 q;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = __float_as_uint(acc[i][e]);
+          dst[v] = q;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const Shape& s, int t0, int t1, const void* hidden,
+                          const int32_t* dst_row, void* x_perm, hipStream_t st) {
+  if (t1 <= t0) return hipSuccess;
+  const int nvec = (int)((int64_t)s.H * s.elem / 16);
+  const unsigned blocks = (unsigned)((t1 - t0 + kWavesPerBlock - 1) / kWavesPerBlock);
+  hipLaunchKernelGGL(permute_rows, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
+                     (const u32x4*)hidden, dst_row, (u32x4*)x_perm, t0, t1, s.k, nvec);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Shape& s, int t0, int t1, const void* y,
+                          const int32_t* dst_row, const float* w, void* out, hipStream_t st) {
+  if (t1 <= t0) return hipSuccess;
+  const int nvec = (int)((int64_t)s.H * s.elem / 16);
+  const unsigned blocks = (unsigned)((t1 - t0 + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (s.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_rows<true>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
+                       (const u32x4*)y, dst_row, w, (u32x4*)out, t0, t1, s.k, nvec);
+  else
+    hipLaunchKernelGGL(combine_rows<false>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
+                       (const u32x4*)y, dst_row, w, (u32x4*)out, t0, t1, s.k, nvec);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,207 @@
+/*
+ * moe.h -- one MoE layer's token dispatch, expert FFN and combine on a single
+ * AMD Instinct MI355X (gfx950), behind a plain C ABI.
+ *
+ * What the layer computes (MindSpeed Chunk MoE article, sections "核心原理"
+ * (core principle) and the timing-diagram section): routing metadata, then a
+ * permute of hidden_states into an expert-contiguous buffer, then the expert
+ * computation, then an unpermute that returns every token's output to its
+ * original position as the top_k_weights-weighted sum over its k experts.  The
+ * Chunk MoE variant cuts the tokens into N chunks of T_chunk = ceil(T/N)
+ * (same article, "一组关键公式", key formulas) and runs adjacent chunks as a
+ * pair so one chunk's data movement overlaps its neighbour's expert compute.
+ *
+ *   out[t] = sum_{j<k} top_k_weights[t][j] * FFN_{top_k_index[t][j]}(hidden_states[t])
+ *   FFN_e(x) = W_down[e] (silu(W_gate[e] x) * (W_up[e] x)),  silu(z) = z / (1 + e^-z)
+ *
+ * The expert FFN form (SwiGLU, no bias) is not spelled out on the pages; it is
+ * the reading this library takes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as tensors are DEVICE memory owned by the caller.  The
+ *    library allocates no device memory and keeps no pointer after it returns.
+ *    Its only state is a per-thread cache of two HIP events per device, used by
+ *    moe_chunked_forward to order its two streams.
+ *  - Calls only enqueue work on the given stream(s) and return.  No call waits
+ *    on the device or copies anything back to the host.
+ *  - Row-major, dense layouts:
+ *      hidden_states, out       [T][H]
+ *      top_k_index              [T][k]  int32
+ *      top_k_weights            [T][k]  float32 (kept in fp32 for every dtype)
+ *      w_gate_up                [E][2I][H]  rows 0..I-1 gate, rows I..2I-1 up
+ *      w_down                   [E][H][I]
+ *    Flat assignment index f = t*k + j.
+ *  - dtype MOE_BF16: hidden_states, weights, out and the intermediates are
+ *    bf16, products accumulate in fp32, and act, y and out are each rounded to
+ *    bf16 (nearest even) exactly once.  dtype MOE_F32: fp32 everywhere.
+ *  - Errors: the status comes from host-side checks of the arguments and of the
+ *    kernel launches; nothing throws across the ABI.  Expert ids outside [0, E)
+ *    are a device-side condition: such slots are dropped (no row, zero
+ *    contribution) and counted into *dev_error.
+ *  - Alignment: tensors of hidden/weight/intermediate/out type and the
+ *    workspace need 16-byte alignment (the workspace 256); int32/float32 arrays
+ *    need 4 bytes.
+ *  - Limits: T >= 0, 1 <= k <= 64, 1 <= E <= 1024, E % G == 0, T*k < 2^31.
+ *    MOE_BF16 needs H % 64 == 0 and I % 64 == 0; MOE_F32 needs H % 4 == 0 and
+ *    I % 4 == 0.  Anything else returns MOE_ERR_UNSUPPORTED or
+ *    MOE_ERR_INVALID_ARG.
+ *  - The library is thread-safe; calls that share output or workspace memory
+ *    must be ordered by the caller.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,          /* null/misaligned pointer, bad size, chunk out of range */
+  MOE_ERR_UNSUPPORTED = 2,          /* valid but outside this build's shape limits */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below what the *_workspace_size call returns */
+  MOE_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem shape.  Field names follow the pages' notation. */
+typedef struct moe_shape {
+  int32_t num_tokens;    /* T: tokens of this GPU's share */
+  int32_t hidden;        /* H: hidden size */
+  int32_t num_experts;   /* E: routed experts */
+  int32_t top_k;         /* k: experts per token */
+  int32_t intermediate;  /* I: expert FFN intermediate size */
+  int32_t num_groups;    /* G: destination groups of E/G contiguous experts (0 means 1) */
+  int32_t num_chunks;    /* N: Chunk MoE chunk count (<= 0 means 1; N > T is legal) */
+  int32_t dtype;         /* moe_dtype */
+} moe_shape;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status status);
+
+/*
+ * Chunk count from the two knobs of the Chunk MoE guide (MindSpeed Chunk MoE
+ * article, "操作指南" step 3): set only one of num_chunks and chunk_size; if
+ * both are > 0, num_chunks wins and *warned (nullable) is set to 1; chunk_size
+ * alone gives ceil(T / chunk_size); neither gives 1.  Host-only, no HIP call.
+ */
+int32_t moe_resolve_num_chunks(int32_t num_tokens, int32_t num_chunks, int32_t chunk_size,
+                               int32_t* warned);
+
+/*
+ * Token range [*t0, *t1) of chunk `chunk`: T_chunk = ceil(T/N) tokens per chunk
+ * (MindSpeed Chunk MoE article, key formulas); trailing chunks may be empty.
+ * Host-only, no HIP call.
+ */
+moe_status moe_chunk_range(const moe_shape* shape, int32_t chunk, int32_t* t0, int32_t* t1);
+
+/* Bytes of scratch moe_route_meta needs.  Host-only. */
+moe_status moe_route_meta_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/*
+ * Bytes of workspace moe_chunked_forward needs: the metadata of all chunks plus
+ * min(N, 2) slots of ceil(T/N)*k rows of (H + I) elements -- the pair
+ * residency W_pair = O(2 x ceil(T/N)) of the Chunk MoE key formulas.  Host-only.
+ */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/*
+ * Routing metadata for ALL chunks in one pass (MindSpeed Chunk MoE article,
+ * timing-diagram section: the metadata of every chunk is produced at once;
+ * MindSpore news page, "# 02 AlltoAllV收发异构复用特性": the per-destination
+ * send lists stay on the device and are reused by combine).
+ *
+ *  top_k_index   [T][k] int32 (in)
+ *  counts        [N][E]   int32 (out): assignments of chunk c routed to expert e
+ *  offsets       [N][E+1] int32 (out): exclusive prefix of counts; offsets[c][E] = valid rows
+ *  group_splits  [N][G]   int32 (out): rows chunk c sends to destination group g
+ *  src_row       [T*k]    int32 (out): src_row[t0_c*k + r] = flat index held by chunk row r,
+ *                                      -1 past the chunk's valid rows
+ *  dst_row       [T*k]    int32 (out): chunk-local row of assignment f, -1 if dropped
+ *  dev_error     [1]      int32 (out, nullable): number of dropped (out-of-range) ids
+ *  ws, ws_bytes  scratch of moe_route_meta_workspace_size bytes
+ *
+ * Rows are stable: inside one expert they keep ascending f.  Every output is an
+ * exact integer result.
+ */
+moe_status moe_route_meta(const moe_shape* shape, const int32_t* top_k_index, int32_t* counts,
+                          int32_t* offsets, int32_t* group_splits, int32_t* src_row,
+                          int32_t* dst_row, int32_t* dev_error, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Permute of chunk `chunk` (MindSpeed Chunk MoE article, core principle):
+ * x_perm[dst_row[f]] = hidden_states[f / k] for every assignment f of the chunk
+ * with dst_row[f] >= 0.  hidden_states and dst_row are the full [T][H] and
+ * [T*k] arrays; x_perm is the chunk's buffer of at least (t1-t0)*k rows of H.
+ * Rows past offsets[chunk][E] are not written.  Pure data movement (bit-exact).
+ */
+moe_status moe_permute(const moe_shape* shape, int32_t chunk, const void* hidden_states,
+                       const int32_t* dst_row, void* x_perm, hipStream_t stream);
+
+/*
+ * First expert GEMM with the SwiGLU epilogue, grouped by expert:
+ * act[r][i] = silu(g) * u with g = x_perm[r] . w_gate_up[e][i],
+ * u = x_perm[r] . w_gate_up[e][I+i], for the rows r in
+ * [offsets[chunk][e], offsets[chunk][e+1]).  offsets is the full [N][E+1]
+ * array; act is the chunk's [rows][I] buffer.  Group sizes are read on the
+ * device; the grid is bounded from (t1-t0)*k.
+ */
+moe_status moe_expert_gate_up(const moe_shape* shape, int32_t chunk, const void* x_perm,
+                              const int32_t* offsets, const void* w_gate_up, void* act,
+                              hipStream_t stream);
+
+/*
+ * Second expert GEMM, grouped by expert: y[r] = act[r] . w_down[e]^T for the
+ * rows of expert e.  y is the chunk's [rows][H] buffer and may alias x_perm.
+ */
+moe_status moe_expert_down(const moe_shape* shape, int32_t chunk, const void* act,
+                           const int32_t* offsets, const void* w_down, void* y,
+                           hipStream_t stream);
+
+/* moe_expert_gate_up followed by moe_expert_down on the same stream. */
+moe_status moe_expert_ffn(const moe_shape* shape, int32_t chunk, const void* x_perm,
+                          const int32_t* offsets, const void* w_gate_up, const void* w_down,
+                          void* act, void* y, hipStream_t stream);
+
+/*
+ * Unpermute and weighted combine of chunk `chunk` (MindSpeed Chunk MoE article,
+ * timing-diagram section; the combine reuses dispatch's dst_row, as the
+ * MindSpore page's "# 02" reuses the dispatch lists):
+ * out[t] = sum_{j<k, dst_row[t*k+j] >= 0} top_k_weights[t][j] * y[dst_row[t*k+j]],
+ * summed in fp32 in ascending j and rounded once.  Writes out rows [t0, t1)
+ * only; a token whose slots were all dropped gets zeros.
+ */
+moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const void* y,
+                                 const int32_t* dst_row, const float* top_k_weights, void* out,
+                                 hipStream_t stream);
+
+/*
+ * The whole layer, Chunk MoE schedule (MindSpeed Chunk MoE article: timing
+ * diagram and key formulas; Ascend dual-stream article, "01 Prefill
+ * micro-batch" overlap of one micro-batch's compute with another's transfer).
+ *
+ * Metadata for all chunks runs once on s0.  Chunk c then runs permute ->
+ * gate_up -> down -> combine on stream s[c % 2] in workspace slot c % 2, so the
+ * two chunks of a pair are in flight together and at most two chunks are
+ * resident.  s1 == s0 is legal and gives the same bits without overlap; the
+ * result never depends on N.  On return s0 is ordered after all work of the
+ * call.  ws must hold moe_workspace_size bytes.  dev_error is nullable.
+ */
+moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states,
+                               const int32_t* top_k_index, const float* top_k_weights,
+                               const void* w_gate_up, const void* w_down, void* out,
+                               int32_t* dev_error, void* ws, size_t ws_bytes, hipStream_t s0,
+                               hipStream_t s1);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

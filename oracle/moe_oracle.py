@@ -46,7 +46,7 @@ import numpy as np
 
 __all__ = [
     "chunk_bounds", "resolve_num_chunks", "w_pair_rows", "route_meta", "permute",
-    "silu", "expert_ffn", "unpermute_combine", "moe_forward", "moe_tokens",
+    "silu", "expert_act", "expert_ffn", "unpermute_combine", "moe_forward", "moe_tokens",
 ]
 
 
@@ -170,12 +170,17 @@ def expert_ffn(x_perm: np.ndarray, offsets_c: Sequence[int], get_expert: ExpertG
         if hi == lo:
             continue
         wgu, wd = get_expert(e)
-        xs = x_perm[lo:hi]
-        gate = xs @ wgu[:I].T
-        up = xs @ wgu[I:2 * I].T
-        act = silu(gate) * up
-        y[lo:hi] = act @ wd.T
+        y[lo:hi] = expert_act(x_perm[lo:hi], wgu, I) @ wd.T
     return y
+
+
+def expert_act(xs: np.ndarray, wgu: np.ndarray, I: int) -> np.ndarray:
+    """SwiGLU activation of one expert's rows: silu(xs W_g^T) * (xs W_u^T), with
+    W_g = wgu[:I] and W_u = wgu[I:2I]."""
+    xs = np.asarray(xs, np.float64)
+    gate = xs @ wgu[:I].T
+    up = xs @ wgu[I:2 * I].T
+    return silu(gate) * up
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,305 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Integer outputs (counts, offsets, splits, src_row, dst_row, dropped-id count)
+and the permute are compared bit-exactly.  Floating outputs are compared with
+the row-wise inf-norm relative error
+    max_t ||gpu_t - oracle_t||_inf / max(||oracle_t||_inf, 1e-30)
+against 1e-5 for fp32 workloads and 2e-2 for bf16 workloads (fp32 accumulate,
+act / y / out each rounded to bf16 once).  GPU chunked output must equal GPU
+unchunked output bit for bit.  Small workloads are compared on every row; the
+large ones on every metadata entry, every permuted row, and sampled experts and
+tokens that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_top_route_expert_amd as moe
+import oracle
+import synth
+from gpu_layer import build_layer, f64, run_forward, run_route_meta, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+C = synth.CONFIGS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+
+
+_layers = {}
+
+
+def layer_for(name, T=None):
+    key = (name, T)
+    if key not in _layers:
+        if len(_layers) > 3:
+            _layers.clear()
+        cfg = C[name] if T is None else C[name].with_tokens(T)
+        _layers[key] = build_layer(cfg)
+    return _layers[key]
+
+
+def sample_tokens(T, n=6, seed=0):
+    rng = np.random.default_rng(seed)
+    base = {0, T - 1, T // 2}
+    base.update(int(x) for x in rng.integers(0, T, size=max(0, n - 3)))
+    return sorted(base)
+
+
+# --------------------------------------------------------------------- inputs
+def test_generator_same_bits_on_device():
+    key = synth.stream_key(3, synth.S_W_GATE_UP, 5)
+    for n, start in [(1000, 0), (1 << 20, 77)]:
+        say(f"generator normal n={n}")
+        assert torch.equal(synth.normal(key, n, 0.02, "cuda", start).cpu(),
+                           synth.normal(key, n, 0.02, "cpu", start))
+    assert torch.equal(synth.uniform(key, 5000, "cuda").cpu(), synth.uniform(key, 5000, "cpu"))
+    cfg = C["bf16_e64_zipf"]
+    assert torch.equal(synth.expert_gate_up(cfg, 3, "cuda").cpu(),
+                       synth.expert_gate_up(cfg, 3, "cpu"))
+    assert torch.equal(synth.hidden_states(cfg.with_tokens(64), "cuda").cpu(),
+                       synth.hidden_states(cfg.with_tokens(64), "cpu"))
+
+
+# --------------------------------------------------------------------- a1 metadata
+META_CASES = [
+    ("tiny_f32", 1, None), ("bf16_e64_zipf", 1, None), ("bf16_e64_zipf", 2, None),
+    ("dsv3_e256", 1, 16), ("dsv3_e256", 1, 8), ("dsv3_e256", 3, 16),
+    ("packed16k_e128", 1, None), ("packed16k_e128", 2, None), ("packed16k_e128", 4, None),
+    ("packed16k_e128", 8, None), ("decode_t64", 1, 16), ("t3_n4", 4, 16), ("t3_n4", 1, 16),
+    ("skew_two_experts", 1, 16),
+]
+
+
+def _check_meta(idx_np, E, G, N, T, k, H=128, I=256, dtype="f32"):
+    shape = moe.make_shape(T, H, E, k, I, G, N, dtype)
+    say(f"route_meta T={T} k={k} E={E} G={G} N={N}")
+    got = run_route_meta(torch.from_numpy(np.ascontiguousarray(idx_np, np.int32)).cuda()
+                         if T else torch.empty(0, dtype=torch.int32, device="cuda"), shape)
+    want = oracle.route_meta(np.asarray(idx_np).reshape(T, k), E, G, N)
+    for key in ("counts", "offsets", "group_splits", "src_row", "dst_row"):
+        assert np.array_equal(got[key].reshape(want[key].shape), want[key]), key
+    assert int(got["dev_error"][0]) == want["n_invalid"]
+
+
+@pytest.mark.parametrize("name,N,G", META_CASES)
+def test_route_meta_bit_exact(name, N, G):
+    cfg = C[name]
+    idx_np, _ = synth.routing(cfg)
+    _check_meta(idx_np, cfg.E, cfg.groups if G is None else G, N, cfg.T, cfg.k, cfg.H, cfg.I,
+                cfg.dtype)
+
+
+@pytest.mark.parametrize("T,k,E,G,N,bad", [
+    (777, 3, 6, 3, 5, 0.1),      # E not a power of two, dropped ids, ragged chunks
+    (100, 64, 1024, 16, 1, 0.0),  # largest k and E
+    (4000, 2, 1, 1, 3, 0.05),    # one expert
+    (3, 8, 256, 16, 7, 0.0),     # more chunks than tokens
+    (1, 1, 8, 1, 1, 0.0),
+    (2500, 8, 256, 16, 2, 1.0),  # every id dropped
+    (0, 8, 256, 16, 4, 0.0),     # no tokens
+])
+def test_route_meta_edge_cases(T, k, E, G, N, bad):
+    rng = np.random.default_rng(T + k + E)
+    idx = rng.integers(0, E, size=(T, k))
+    if bad:
+        m = rng.random((T, k)) < bad
+        idx[m] = rng.choice([-1, E, E + 3, -(1 << 30)], size=int(m.sum()))
+    _check_meta(idx.astype(np.int32), E, G, N, T, k)
+
+
+# --------------------------------------------------------------------- a2 permute
+@pytest.mark.parametrize("name,N", [("tiny_f32", 1), ("bf16_e64_zipf", 2), ("dsv3_e256", 1),
+                                    ("packed16k_e128", 4), ("t3_n4", 4)])
+def test_permute_bit_exact(name, N):
+    L = layer_for(name)
+    cfg = L.cfg
+    shape = L.shape(N)
+    meta = run_route_meta(L.idx, shape)
+    want = oracle.route_meta(L.idx_np, cfg.E, shape.G, N)
+    dst = torch.from_numpy(meta["dst_row"]).cuda()
+    for c in range(N):
+        t0, t1 = moe.moe_chunk_range(shape, c)
+        rows = (t1 - t0) * cfg.k
+        valid = int(want["offsets"][c, cfg.E])
+        # one canary row past the chunk's rows
+        xp = torch.empty((rows + 1, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+        xp.view(torch.int16 if cfg.dtype == "bf16" else torch.int32).fill_(-12345)
+        say(f"permute {name} N={N} chunk={c}")
+        moe.moe_permute(shape, c, L.hidden, dst, xp)
+        torch.cuda.synchronize()
+        src = torch.from_numpy(want["src_row"][t0 * cfg.k:t0 * cfg.k + valid] // cfg.k).cuda()
+        expect = L.hidden.index_select(0, src.long())  # the oracle's permutation applied
+        assert torch.equal(xp[:valid], expect)
+        canary = xp[valid:].view(torch.int16 if cfg.dtype == "bf16" else torch.int32)
+        assert bool((canary == -12345).all())
+
+
+# --------------------------------------------------------------------- a3/a4 expert FFN
+def _chunk_pipeline(L, shape, c):
+    """GPU route_meta + permute + gate_up + down for one chunk, through the C ABI."""
+    cfg = L.cfg
+    meta = run_route_meta(L.idx, shape)
+    t0, t1 = moe.moe_chunk_range(shape, c)
+    rows = (t1 - t0) * cfg.k
+    dst = torch.from_numpy(meta["dst_row"]).cuda()
+    off = torch.from_numpy(meta["offsets"]).cuda()
+    xp = torch.zeros((rows, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+    act = torch.zeros((rows, cfg.I), dtype=cfg.torch_dtype, device="cuda")
+    y = torch.zeros((rows, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+    say(f"expert ffn {cfg.name} N={shape.N} chunk={c}")
+    moe.moe_permute(shape, c, L.hidden, dst, xp)
+    moe.moe_expert_gate_up(shape, c, xp, off, L.wgu, act)
+    moe.moe_expert_down(shape, c, act, off, L.wd, y)
+    torch.cuda.synchronize()
+    return meta, act, y
+
+
+@pytest.mark.parametrize("name,N,n_experts", [
+    ("tiny_f32", 1, None), ("bf16_e64_zipf", 2, 6), ("dsv3_e256", 1, 3),
+    ("packed16k_e128", 2, 4), ("skew_two_experts", 1, 2), ("decode_t64", 1, 4),
+])
+def test_expert_ffn_vs_oracle(name, N, n_experts):
+    L = layer_for(name)
+    cfg = L.cfg
+    shape = L.shape(N)
+    c = N - 1  # the last chunk: ragged when T % N != 0
+    meta, act, y = _chunk_pipeline(L, shape, c)
+    want = oracle.route_meta(L.idx_np, cfg.E, shape.G, N)
+    t0, _ = moe.moe_chunk_range(shape, c)
+    off = want["offsets"][c]
+    active = [e for e in range(cfg.E) if off[e + 1] > off[e]]
+    if n_experts is not None:
+        # the largest expert, the smallest, and evenly spaced others
+        by_size = sorted(active, key=lambda e: off[e + 1] - off[e])
+        pick = {by_size[0], by_size[-1]}
+        pick.update(by_size[i] for i in np.linspace(0, len(by_size) - 1, n_experts).astype(int))
+        active = sorted(pick)
+    hid = L.hidden64()
+    tol = TOL[cfg.dtype]
+    for e in active:
+        lo, hi = int(off[e]), int(off[e + 1])
+        xs = oracle.permute(hid, want["src_row"][t0 * cfg.k + lo:t0 * cfg.k + hi], cfg.k, hi - lo)
+        wgu, wd = L.expert64(e)
+        ref_act = oracle.expert_act(xs, wgu, cfg.I)
+        ref_y = oracle.expert_ffn(xs, [0, hi - lo], lambda _: (wgu, wd), cfg.I)
+        err_a = oracle.row_rel_err(f64(act[lo:hi]), ref_act)
+        err_y = oracle.row_rel_err(f64(y[lo:hi]), ref_y)
+        assert err_a <= tol, (e, err_a)
+        assert err_y <= tol, (e, err_y)
+
+
+# --------------------------------------------------------------------- whole layer
+FULL_CASES = [("tiny_f32", 1, None), ("t3_n4", 4, None), ("t3_n4", 1, None),
+              ("bf16_e64_zipf", 1, 1024), ("bf16_e64_zipf", 2, 1000)]
+
+
+@pytest.mark.parametrize("name,N,T", FULL_CASES)
+def test_forward_every_row_vs_oracle(name, N, T):
+    L = layer_for(name, T)
+    cfg = L.cfg
+    out, err = run_forward(L, L.shape(N))
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, N)
+    assert err == meta["n_invalid"] == 0
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL[cfg.dtype], e
+
+
+SAMPLED_CASES = [("bf16_e64_zipf", 2, 24), ("dsv3_e256", 1, 4), ("packed16k_e128", 4, 48),
+                 ("packed16k_e128", 8, 16), ("decode_t64", 1, 6), ("skew_two_experts", 1, 64)]
+
+
+@pytest.mark.parametrize("name,N,n_tok", SAMPLED_CASES)
+def test_forward_sampled_tokens_vs_oracle(name, N, n_tok):
+    L = layer_for(name)
+    cfg = L.cfg
+    out, err = run_forward(L, L.shape(N))
+    assert err == 0
+    toks = sample_tokens(cfg.T, n_tok)
+    ref = oracle.moe_tokens(toks, L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I)
+    e = oracle.row_rel_err(f64(out[toks]), ref)
+    assert e <= TOL[cfg.dtype], e
+    assert not torch.isnan(out.float()).any()
+
+
+@pytest.mark.parametrize("name,Ns", [("bf16_e64_zipf", (2,)), ("packed16k_e128", (2, 4, 8)),
+                                     ("t3_n4", (4,)), ("dsv3_e256", (3,)),
+                                     ("tiny_f32", (2, 5))])
+def test_chunked_equals_unchunked_bitwise(name, Ns):
+    L = layer_for(name)
+    base, _ = run_forward(L, L.shape(1), two_streams=False)
+    for N in Ns:
+        for two in (True, False):
+            say(f"chunked {name} N={N} two_streams={two}")
+            out, _ = run_forward(L, L.shape(N), two_streams=two)
+            assert torch.equal(out, base), (N, two)
+
+
+def test_run_twice_identical():
+    L = layer_for("packed16k_e128")
+    a, _ = run_forward(L, L.shape(2))
+    b, _ = run_forward(L, L.shape(2))
+    assert torch.equal(a, b)
+
+
+def test_steps_compose_to_forward():
+    """route_meta + per-chunk permute / gate_up / down / combine == chunked_forward."""
+    L = layer_for("bf16_e64_zipf")
+    cfg = L.cfg
+    shape = L.shape(2)
+    fwd, _ = run_forward(L, shape)
+    meta = run_route_meta(L.idx, shape)
+    dst = torch.from_numpy(meta["dst_row"]).cuda()
+    off = torch.from_numpy(meta["offsets"]).cuda()
+    out = torch.zeros_like(fwd)
+    for c in range(2):
+        t0, t1 = moe.moe_chunk_range(shape, c)
+        rows = (t1 - t0) * cfg.k
+        xp = torch.empty((rows, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+        act = torch.empty((rows, cfg.I), dtype=cfg.torch_dtype, device="cuda")
+        moe.moe_permute(shape, c, L.hidden, dst, xp)
+        moe.moe_expert_ffn(shape, c, xp, off, L.wgu, L.wd, act, xp)
+        moe.moe_unpermute_combine(shape, c, xp, dst, L.w, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fwd)
+
+
+def test_dropped_ids_and_canary_rows():
+    """Out-of-range ids are dropped and counted; a token with every slot dropped
+    gets zeros; rows past T are never written."""
+    cfg = C["tiny_f32"]
+    idx, w = synth.routing(cfg)
+    idx = idx.copy()
+    idx[5, :] = -1
+    idx[9, 1] = cfg.E
+    idx[200, 0] = 1 << 20
+    L = build_layer(cfg, idx, w)
+    for N in (1, 3):
+        out = torch.full((cfg.T + 2, cfg.H), 777.0, dtype=cfg.torch_dtype, device="cuda")
+        got, err = run_forward(L, L.shape(N), out=out)
+        ref, meta = oracle.moe_forward(L.hidden64(), idx, w, L.expert64, cfg.E, cfg.I, 1, N)
+        assert err == meta["n_invalid"] == cfg.k + 2
+        assert oracle.row_rel_err(f64(got[:cfg.T]), ref) <= TOL["f32"]
+        assert bool((got[5] == 0).all())
+        assert bool((got[cfg.T:] == 777.0).all())
+
+
+def test_zero_tokens():
+    cfg = C["tiny_f32"].with_tokens(0)
+    shape = moe.make_shape(0, cfg.H, cfg.E, cfg.k, cfg.I, 1, 3, cfg.dtype)
+    ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    err = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    z = torch.empty(0, device="cuda")
+    say("zero tokens")
+    moe.moe_chunked_forward(shape, z, torch.empty(0, dtype=torch.int32, device="cuda"), z,
+                            torch.zeros(cfg.E * 2 * cfg.I * cfg.H, device="cuda"),
+                            torch.zeros(cfg.E * cfg.H * cfg.I, device="cuda"), z, ws, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
