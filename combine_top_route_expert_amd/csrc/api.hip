@@ -112,7 +112,7 @@ moe_status resolve_shape(const moe_shape* in, Shape* s) {
   const int G = in->num_groups <= 0 ? 1 : in->num_groups;
   if (in->num_experts % G) return MOE_ERR_INVALID_ARG;
   const int N = in->num_chunks <= 0 ? 1 : in->num_chunks;
-  if (in->top_k > 64 || in->num_experts > 1024 || N > kMaxChunks) return MOE_ERR_UNSUPPORTED;
+  if (in->top_k > 64 || in->num_experts > kMaxExperts || N > kMaxChunks) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)in->num_tokens * in->top_k > 0x7fffffffLL) return MOE_ERR_UNSUPPORTED;
   if (in->dtype == MOE_BF16) {
     if (in->hidden % 64 || in->intermediate % 64) return MOE_ERR_UNSUPPORTED;

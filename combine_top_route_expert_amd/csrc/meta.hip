@@ -36,7 +36,7 @@ struct MetaArgs {
   int32_t* src_row;
   int32_t* dst_row;
   int32_t* dev_error;
-  int T, k, E, G, N, Tc, spc, id_bits;
+  int T, k, E, G, N, Tc, spc, seg, id_bits;
 };
 
 // Segment `seg` -> its chunk and flat range [f_lo, f_hi).
@@ -46,8 +46,8 @@ __device__ __forceinline__ void seg_range(const MetaArgs& a, int seg, int* chunk
   long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
   if (t0 > a.T) t0 = a.T;
   if (t1 > a.T) t1 = a.T;
-  long long lo = t0 * a.k + (long long)j * kMetaSeg;
-  long long hi = lo + kMetaSeg;
+  long long lo = t0 * a.k + (long long)j * a.seg;
+  long long hi = lo + a.seg;
   if (hi > t1 * a.k) hi = t1 * a.k;
   if (lo > hi) lo = hi;
   *chunk = c;
@@ -67,6 +67,23 @@ __device__ __forceinline__ uint64_t peer_mask(int e, bool ok, int id_bits) {
   return m;
 }
 
+// Ids of one 1024-assignment batch, 16 per lane, loaded together so their
+// latencies overlap; inactive lanes (past the segment) get ok = false.
+struct IdBatch {
+  int e[16];
+  bool active[16];
+};
+
+__device__ __forceinline__ void load_batch(const MetaArgs& a, int b0, int f_hi, int lane,
+                                           IdBatch* b) {
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    const int f = b0 + g * 64 + lane;
+    b->active[g] = f < f_hi;
+    b->e[g] = b->active[g] ? a.idx[f] : -1;
+  }
+}
+
 __global__ void __launch_bounds__(64) meta_hist(MetaArgs a) {
   extern __shared__ int cnt[];
   const int lane = threadIdx.x;
@@ -75,15 +92,18 @@ __global__ void __launch_bounds__(64) meta_hist(MetaArgs a) {
   for (int e = lane; e < a.E; e += 64) cnt[e] = 0;
   __syncthreads();
   int invalid = 0;
-  for (int base = f_lo; base < f_hi; base += 64) {
-    int f = base + lane;
-    bool active = f < f_hi;
-    int e = active ? a.idx[f] : -1;
-    bool ok = active && e >= 0 && e < a.E;
-    invalid += (active && !ok) ? 1 : 0;
-    uint64_t peers = peer_mask(e, ok, a.id_bits);
-    if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) cnt[e] += __popcll(peers);
-    __syncthreads();
+  for (int b0 = f_lo; b0 < f_hi; b0 += 1024) {
+    IdBatch b;
+    load_batch(a, b0, f_hi, lane, &b);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int e = b.e[g];
+      const bool ok = b.active[g] && e >= 0 && e < a.E;
+      invalid += (b.active[g] && !ok) ? 1 : 0;
+      const uint64_t peers = peer_mask(e, ok, a.id_bits);
+      if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) cnt[e] += __popcll(peers);
+      __syncthreads();
+    }
   }
   int32_t* out = a.seg_counts + (size_t)blockIdx.x * a.E;
   for (int e = lane; e < a.E; e += 64) out[e] = cnt[e];
@@ -119,18 +139,22 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds_waves) {
 }
 
 __global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
+  __shared__ int stage[kScanStage];
   __shared__ int lds_waves[48];
   __shared__ int off_lds[1025];
   const int e = threadIdx.x;
   const bool has_e = e < a.E;
   for (int c = 0; c < a.N; ++c) {
     const size_t seg0 = (size_t)c * a.spc;
+    const int n_stage = a.spc * a.E;  // <= kScanStage by the plan
+    int32_t* blk = a.seg_counts + seg0 * a.E;
+    for (int i = threadIdx.x; i < n_stage; i += blockDim.x) stage[i] = blk[i];
+    __syncthreads();
     int run = 0;
     if (has_e) {
       for (int j = 0; j < a.spc; ++j) {
-        int32_t* p = a.seg_counts + (seg0 + j) * a.E + e;
-        int v = *p;
-        *p = run;
+        const int v = stage[j * a.E + e];
+        stage[j * a.E + e] = run;
         run += v;
       }
     }
@@ -140,13 +164,14 @@ __global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
       a.counts[(size_t)c * a.E + e] = run;
       a.offsets[(size_t)c * (a.E + 1) + e] = off;
       off_lds[e] = off;
-      for (int j = 0; j < a.spc; ++j) a.seg_counts[(seg0 + j) * a.E + e] += off;
     }
     if (e == 0) {
       a.offsets[(size_t)c * (a.E + 1) + a.E] = total;
       off_lds[a.E] = total;
     }
     __syncthreads();
+    // segment bases: chunk offset + prefix over the chunk's earlier segments
+    for (int i = threadIdx.x; i < n_stage; i += blockDim.x) blk[i] = stage[i] + off_lds[i % a.E];
     const int per = a.E / a.G;
     for (int g = threadIdx.x; g < a.G; g += blockDim.x)
       a.splits[(size_t)c * a.G + g] = off_lds[(g + 1) * per] - off_lds[g * per];
@@ -178,19 +203,23 @@ __global__ void __launch_bounds__(64) meta_rank(MetaArgs a) {
   for (int e = lane; e < a.E; e += 64) base[e] = sb[e];
   __syncthreads();
   const uint64_t lt = lanemask_lt();
-  for (int b0 = f_lo; b0 < f_hi; b0 += 64) {
-    int f = b0 + lane;
-    bool active = f < f_hi;
-    int e = active ? a.idx[f] : -1;
-    bool ok = active && e >= 0 && e < a.E;
-    uint64_t peers = peer_mask(e, ok, a.id_bits);
-    int row = -1;
-    if (ok) row = base[e] + __popcll(peers & lt);
-    __syncthreads();  // every lane has read base[] before the leaders advance it
-    if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) base[e] += __popcll(peers);
-    if (active) a.dst_row[f] = row;
-    if (ok) a.src_row[cf0 + row] = f;
-    __syncthreads();
+  for (int b0 = f_lo; b0 < f_hi; b0 += 1024) {
+    IdBatch b;
+    load_batch(a, b0, f_hi, lane, &b);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int f = b0 + g * 64 + lane;
+      const int e = b.e[g];
+      const bool ok = b.active[g] && e >= 0 && e < a.E;
+      const uint64_t peers = peer_mask(e, ok, a.id_bits);
+      int row = -1;
+      if (ok) row = base[e] + __popcll(peers & lt);
+      __syncthreads();  // every lane has read base[] before the leaders advance it
+      if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) base[e] += __popcll(peers);
+      if (b.active[g]) a.dst_row[f] = row;
+      if (ok) a.src_row[cf0 + row] = f;
+      __syncthreads();
+    }
   }
 }
 
@@ -204,8 +233,13 @@ int bits_for(int E) {
 
 MetaPlan meta_plan(const Shape& s) {
   MetaPlan p{};
-  int64_t ac = (int64_t)s.Tc * s.k;
-  p.segs_per_chunk = (int)((ac + kMetaSeg - 1) / kMetaSeg);
+  const int64_t ac = (int64_t)s.Tc * s.k;
+  // segment = a multiple of 1024 assignments, large enough that one chunk's
+  // [segments][E] counts fit the scan kernel's LDS block
+  int64_t seg = kMetaSeg;
+  while (((ac + seg - 1) / seg) * s.E > kScanStage) seg += kMetaSeg;
+  p.seg = (int)seg;
+  p.segs_per_chunk = (int)((ac + seg - 1) / seg);
   if (p.segs_per_chunk < 1) p.segs_per_chunk = 1;
   p.nseg = (int64_t)s.N * p.segs_per_chunk;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -236,6 +270,7 @@ hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts
   a.N = s.N;
   a.Tc = s.Tc;
   a.spc = p.segs_per_chunk;
+  a.seg = p.seg;
   a.id_bits = bits_for(s.E);
   const size_t lds = (size_t)s.E * sizeof(int);
   hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), lds, st, a);

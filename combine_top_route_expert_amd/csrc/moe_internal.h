@@ -26,9 +26,12 @@ inline void chunk_tokens(const Shape& s, int c, int* t0, int* t1) {
 }
 
 // ---- routing metadata (meta.hip) -------------------------------------------
-constexpr int kMetaSeg = 1024;  // assignments per segment (one wave per segment)
+constexpr int kMaxExperts = 1024;  // largest E the library accepts
+constexpr int kMetaSeg = 1024;     // segment granule, in assignments (one wave per segment)
+constexpr int kScanStage = 16384;  // ints of one chunk's [segments][E] block staged in LDS
 
 struct MetaPlan {
+  int seg;                 // assignments per segment (multiple of kMetaSeg)
   int segs_per_chunk;
   int64_t nseg;            // N * segs_per_chunk
   size_t seg_counts_off;   // int32 [nseg][E]
