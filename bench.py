@@ -2,9 +2,11 @@
 """MoE-layer benchmark on one MI355X.
 
 A step is one moe_chunked_forward call: routing metadata for every chunk,
-then per chunk permute -> gate/up GEMM + SwiGLU -> down GEMM -> weighted
-combine, chunks paired on two HIP streams.  Inputs are seeded synthetic data
-already resident in HBM when the timed region starts.
+then per chunk pair: the two permutes on two HIP streams, one gate/up GEMM +
+SwiGLU launch and one down GEMM launch over both chunks' rows, the two
+weighted combines on two streams.  The per-chunk schedule (every chunk runs
+all four steps on its own stream) is timed beside it.  Inputs are seeded
+synthetic data already resident in HBM when the timed region starts.
 
 Prints ONE JSON line: MoE-layer tokens/s (T / seconds per step), the roofline
 of the dominant kernel (the gate/up grouped GEMM) measured live with HIP
@@ -51,7 +53,8 @@ def make_inputs(cfg, torch, synth):
             "idx_np": idx, "w_np": w, "counts": np.bincount(idx.ravel(), minlength=cfg.E)}
 
 
-def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True):
+def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True,
+               schedule=None):
     cfg_dtype = shape.torch_dtype
     out = torch.empty((shape.T, shape.H), dtype=cfg_dtype, device="cuda")
     ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
@@ -60,8 +63,13 @@ def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True):
     s1 = torch.cuda.Stream() if two_streams else None
 
     def step():
-        moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"],
-                                inp["wd"], out, ws, err, s0=s0, s1=s1)
+        if schedule is None:
+            moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"],
+                                    inp["wd"], out, ws, err, s0=s0, s1=s1)
+        else:
+            moe.moe_chunked_forward_schedule(shape, inp["hidden"], inp["idx"], inp["w"],
+                                             inp["wgu"], inp["wd"], out, ws, err, s0=s0, s1=s1,
+                                             schedule=schedule)
 
     for _ in range(warmup):
         step()
@@ -80,8 +88,10 @@ def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True):
 
 
 def kernel_times(moe, torch, shape, inp, reps):
-    """Average duration of each step's launch on chunk 0, HIP events on the
-    stream the kernels run on (torch's current stream)."""
+    """Average duration of each launch the layer makes for its first chunk pair
+    (route_meta for all chunks; permute and combine of chunk 0; the gate_up and
+    down launches over chunks 0 and 1), HIP events on the stream the kernels
+    run on (torch's current stream)."""
     T, k, E, N, G, H, I = shape.T, shape.k, shape.E, shape.N, shape.G, shape.H, shape.I
     dt = shape.torch_dtype
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -92,20 +102,25 @@ def kernel_times(moe, torch, shape, inp, reps):
     dst_row = torch.empty(T * k, **i32)
     err = torch.empty(1, **i32)
     mws = torch.empty(moe.moe_route_meta_workspace_size(shape), dtype=torch.uint8, device="cuda")
-    t0, t1 = moe.moe_chunk_range(shape, 0)
-    rows = (t1 - t0) * k
-    xp = torch.empty((rows, H), dtype=dt, device="cuda")
-    act = torch.empty((rows, I), dtype=dt, device="cuda")
-    y = torch.empty((rows, H), dtype=dt, device="cuda")
+    rows = []
+    for c in range(min(N, 2)):
+        t0, t1 = moe.moe_chunk_range(shape, c)
+        rows.append((t1 - t0) * k)
+    if len(rows) < 2:
+        rows.append(0)
+    xp = [torch.empty((max(r, 1), H), dtype=dt, device="cuda") for r in rows]
+    act = torch.empty((rows[0] + rows[1], I), dtype=dt, device="cuda")
     out = torch.empty((T, H), dtype=dt, device="cuda")
     s = torch.cuda.current_stream()
+    x1 = xp[1] if rows[1] else None
     calls = {
         "route_meta": lambda: moe.moe_route_meta(shape, inp["idx"], counts, offsets, splits,
                                                  src_row, dst_row, err, mws, s),
-        "permute": lambda: moe.moe_permute(shape, 0, inp["hidden"], dst_row, xp, s),
-        "gate_up": lambda: moe.moe_expert_gate_up(shape, 0, xp, offsets, inp["wgu"], act, s),
-        "down": lambda: moe.moe_expert_down(shape, 0, act, offsets, inp["wd"], y, s),
-        "combine": lambda: moe.moe_unpermute_combine(shape, 0, y, dst_row, inp["w"], out, s),
+        "permute": lambda: moe.moe_permute(shape, 0, inp["hidden"], dst_row, xp[0], s),
+        "gate_up": lambda: moe.moe_expert_gate_up_pair(shape, 0, xp[0], x1, offsets, inp["wgu"],
+                                                       act, s),
+        "down": lambda: moe.moe_expert_down_pair(shape, 0, act, offsets, inp["wd"], xp[0], x1, s),
+        "combine": lambda: moe.moe_unpermute_combine(shape, 0, xp[0], dst_row, inp["w"], out, s),
     }
     res = {}
     for name, fn in calls.items():
@@ -120,8 +135,8 @@ def kernel_times(moe, torch, shape, inp, reps):
         e1.record(s)
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) * 1e3 / reps  # microseconds per launch
-    c0 = counts[0].cpu()
-    return res, int(c0.sum().item()), int((c0 > 0).sum().item()), rows
+    cp = counts[:2].sum(0).cpu()
+    return res, int(cp.sum().item()), int((cp > 0).sum().item()), rows
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
@@ -228,6 +243,9 @@ def main():
     log(f"layer N=1 (reference)")
     shape1 = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, 1, cfg.dtype)
     run1 = time_layer(moe, torch, shape1, inp, args.steps, args.warmup, two_streams=False)
+    log(f"layer N={N}, per-chunk schedule")
+    run_pc = time_layer(moe, torch, shape, inp, args.steps, args.warmup,
+                        schedule=moe.MOE_SCHEDULE_PER_CHUNK)
     log("per-kernel timing")
     kt, rows0, e_act0, _ = kernel_times(moe, torch, shape, inp, args.kernel_reps)
     copy_bw = copy_bandwidth(torch)
@@ -247,7 +265,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     traffic = load_traffic(cfg.name, N)
     roof["traffic"] = traffic
-    roof["kernel"] = "grouped_gemm_bf16<gate_up> (moe_expert_gate_up), chunk 0"
+    roof["kernel"] = ("grouped_gemm_bf16<gate_up> (moe_expert_gate_up_pair), chunks 0-1"
+                      if N >= 2 else "grouped_gemm_bf16<gate_up> (moe_expert_gate_up_pair), chunk 0")
+    roof["rows_per_launch"] = rows0
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["algorithmic_flop_per_launch"] = gu_flops
     roof["avg_launch_us"] = kt["gate_up"]
@@ -261,9 +281,11 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "E": cfg.E, "top_k": cfg.k,
                    "I": I, "num_chunks": N, "streams": 2, "groups": cfg.groups},
         "roofline": roof,
-        "kernels_us_chunk0": kt,
+        "kernels_us": kt,
         "event_ms_per_step": main_run["event_ms"],
         "unchunked": {"ms_per_step": run1["wall_ms"], "value": cfg.T / (run1["wall_ms"] * 1e-3)},
+        "per_chunk_schedule": {"ms_per_step": run_pc["wall_ms"],
+                               "value": cfg.T / (run_pc["wall_ms"] * 1e-3)},
         "workspace_bytes": {"N": main_run["workspace_bytes"], "N1": run1["workspace_bytes"]},
         "copy_bandwidth_GBps": copy_bw / 1e9,
         "expert_load": {"max_over_mean": float(inp["counts"].max() / inp["counts"].mean()),

@@ -20,19 +20,23 @@ __all__ = [
     "MoeError", "moe_shape", "make_shape", "library_path", "load_library", "moe_status_string",
     "moe_resolve_num_chunks", "moe_chunk_range", "moe_route_meta_workspace_size",
     "moe_workspace_size", "moe_route_meta", "moe_permute", "moe_expert_gate_up",
-    "moe_expert_down", "moe_expert_ffn", "moe_unpermute_combine", "moe_chunked_forward",
-    "MOE_F32", "MOE_BF16", "EXPORTED_SYMBOLS",
+    "moe_expert_down", "moe_expert_ffn", "moe_expert_ffn_pair", "moe_expert_gate_up_pair",
+    "moe_expert_down_pair", "moe_unpermute_combine", "moe_chunked_forward",
+    "moe_chunked_forward_schedule", "MOE_F32", "MOE_BF16",
+    "MOE_SCHEDULE_PAIR_FUSED", "MOE_SCHEDULE_PER_CHUNK", "EXPORTED_SYMBOLS",
 ]
 
 MOE_F32, MOE_BF16 = 0, 1
+MOE_SCHEDULE_PAIR_FUSED, MOE_SCHEDULE_PER_CHUNK = 0, 1
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_resolve_num_chunks", "moe_chunk_range",
     "moe_route_meta_workspace_size", "moe_workspace_size", "moe_route_meta", "moe_permute",
-    "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_unpermute_combine",
-    "moe_chunked_forward",
+    "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_expert_gate_up_pair",
+    "moe_expert_down_pair", "moe_expert_ffn_pair", "moe_unpermute_combine",
+    "moe_chunked_forward", "moe_chunked_forward_schedule",
 )
 
 
@@ -113,9 +117,17 @@ def load_library() -> ctypes.CDLL:
         "moe_expert_gate_up": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P]),
         "moe_expert_down": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P]),
         "moe_expert_ffn": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
+        "moe_expert_gate_up_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                                   _P]),
+        "moe_expert_down_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+        "moe_expert_ffn_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                               _P, _P, _P]),
         "moe_unpermute_combine": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P]),
         "moe_chunked_forward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P,
                                                ctypes.c_size_t, _P, _P]),
+        "moe_chunked_forward_schedule": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                        ctypes.c_size_t, _P, _P,
+                                                        ctypes.c_int32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -258,6 +270,54 @@ def moe_expert_ffn(shape: moe_shape, chunk: int, x_perm, offsets, w_gate_up, w_d
         _stream(stream)))
 
 
+def _pair_rows(shape: moe_shape, chunk: int) -> Tuple[int, int]:
+    rows0 = _chunk_rows(shape, chunk)[2]
+    rows1 = _chunk_rows(shape, chunk + 1)[2] if chunk + 1 < shape.N else 0
+    return rows0, rows1
+
+
+def moe_expert_gate_up_pair(shape: moe_shape, chunk: int, x_perm0, x_perm1, offsets, w_gate_up,
+                            act, stream=None) -> None:
+    rows0, rows1 = _pair_rows(shape, chunk)
+    dt = shape.torch_dtype
+    _check("moe_expert_gate_up_pair", load_library().moe_expert_gate_up_pair(
+        ctypes.byref(shape), chunk, _ptr(x_perm0, dt, rows0 * shape.H, "x_perm0"),
+        _ptr(x_perm1, dt, rows1 * shape.H, "x_perm1"),
+        _ptr(offsets, torch.int32, shape.N * (shape.E + 1), "offsets"),
+        _ptr(w_gate_up, dt, shape.E * 2 * shape.I * shape.H, "w_gate_up"),
+        _ptr(act, dt, (rows0 + rows1) * shape.I, "act"), _stream(stream)))
+
+
+def moe_expert_down_pair(shape: moe_shape, chunk: int, act, offsets, w_down, y0, y1,
+                         stream=None) -> None:
+    rows0, rows1 = _pair_rows(shape, chunk)
+    dt = shape.torch_dtype
+    _check("moe_expert_down_pair", load_library().moe_expert_down_pair(
+        ctypes.byref(shape), chunk, _ptr(act, dt, (rows0 + rows1) * shape.I, "act"),
+        _ptr(offsets, torch.int32, shape.N * (shape.E + 1), "offsets"),
+        _ptr(w_down, dt, shape.E * shape.H * shape.I, "w_down"),
+        _ptr(y0, dt, rows0 * shape.H, "y0"), _ptr(y1, dt, rows1 * shape.H, "y1"),
+        _stream(stream)))
+
+
+def moe_expert_ffn_pair(shape: moe_shape, chunk: int, x_perm0, x_perm1, offsets, w_gate_up,
+                        w_down, act, y0, y1, stream=None) -> None:
+    """FFN of chunks `chunk` and `chunk + 1` in one launch pair; `act` holds the
+    pair's rows grouped by expert.  x_perm1/y1 may be None when the second chunk
+    does not exist or is empty."""
+    rows0, rows1 = _pair_rows(shape, chunk)
+    dt = shape.torch_dtype
+    _check("moe_expert_ffn_pair", load_library().moe_expert_ffn_pair(
+        ctypes.byref(shape), chunk, _ptr(x_perm0, dt, rows0 * shape.H, "x_perm0"),
+        _ptr(x_perm1, dt, rows1 * shape.H, "x_perm1"),
+        _ptr(offsets, torch.int32, shape.N * (shape.E + 1), "offsets"),
+        _ptr(w_gate_up, dt, shape.E * 2 * shape.I * shape.H, "w_gate_up"),
+        _ptr(w_down, dt, shape.E * shape.H * shape.I, "w_down"),
+        _ptr(act, dt, (rows0 + rows1) * shape.I, "act"),
+        _ptr(y0, dt, rows0 * shape.H, "y0"), _ptr(y1, dt, rows1 * shape.H, "y1"),
+        _stream(stream)))
+
+
 def moe_unpermute_combine(shape: moe_shape, chunk: int, y, dst_row, top_k_weights, out,
                           stream=None) -> None:
     _, _, rows = _chunk_rows(shape, chunk)
@@ -269,17 +329,29 @@ def moe_unpermute_combine(shape: moe_shape, chunk: int, y, dst_row, top_k_weight
         _ptr(out, dt, shape.T * shape.H, "out"), _stream(stream)))
 
 
-def moe_chunked_forward(shape: moe_shape, hidden_states, top_k_index, top_k_weights, w_gate_up,
-                        w_down, out, ws, dev_error=None, s0=None, s1=None) -> None:
+def moe_chunked_forward_schedule(shape: moe_shape, hidden_states, top_k_index, top_k_weights,
+                                 w_gate_up, w_down, out, ws, dev_error=None, s0=None, s1=None,
+                                 schedule: int = MOE_SCHEDULE_PAIR_FUSED,
+                                 _fn: str = "moe_chunked_forward_schedule") -> None:
     dt = shape.torch_dtype
     T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I  # noqa: E741
     wp, wn = _ws_ptr(ws, moe_workspace_size(shape))
     s0i = _stream(s0)
     s1i = _stream(s1) if s1 is not None else None
-    _check("moe_chunked_forward", load_library().moe_chunked_forward(
-        ctypes.byref(shape), _ptr(hidden_states, dt, T * H, "hidden_states"),
-        _ptr(top_k_index, torch.int32, T * k, "top_k_index"),
-        _ptr(top_k_weights, torch.float32, T * k, "top_k_weights"),
-        _ptr(w_gate_up, dt, E * 2 * I * H, "w_gate_up"), _ptr(w_down, dt, E * H * I, "w_down"),
-        _ptr(out, dt, T * H, "out"), _ptr(dev_error, torch.int32, 0, "dev_error"), wp, wn, s0i,
-        s1i))
+    args = (ctypes.byref(shape), _ptr(hidden_states, dt, T * H, "hidden_states"),
+            _ptr(top_k_index, torch.int32, T * k, "top_k_index"),
+            _ptr(top_k_weights, torch.float32, T * k, "top_k_weights"),
+            _ptr(w_gate_up, dt, E * 2 * I * H, "w_gate_up"), _ptr(w_down, dt, E * H * I, "w_down"),
+            _ptr(out, dt, T * H, "out"), _ptr(dev_error, torch.int32, 0, "dev_error"), wp, wn,
+            s0i, s1i)
+    lib = load_library()
+    if _fn == "moe_chunked_forward":
+        _check(_fn, lib.moe_chunked_forward(*args))
+    else:
+        _check(_fn, lib.moe_chunked_forward_schedule(*args, schedule))
+
+
+def moe_chunked_forward(shape: moe_shape, hidden_states, top_k_index, top_k_weights, w_gate_up,
+                        w_down, out, ws, dev_error=None, s0=None, s1=None) -> None:
+    moe_chunked_forward_schedule(shape, hidden_states, top_k_index, top_k_weights, w_gate_up,
+                                 w_down, out, ws, dev_error, s0, s1, _fn="moe_chunked_forward")

@@ -1,5 +1,5 @@
 // C-ABI entry points: argument checks, workspace planning and the Chunk MoE
-// two-stream schedule.  Every function only enqueues work; none synchronises
+// two-stream schedules.  Every function only enqueues work; none synchronises
 // with the device or copies anything to the host.
 #include <mutex>
 #include <vector>
@@ -44,41 +44,49 @@ FwdPlan fwd_plan(const Shape& s) {
   p.meta_ws = take(p.meta.bytes);
   const size_t rows = (size_t)s.Tc * s.k;
   p.nslots = s.N >= 2 ? 2 : 1;
-  for (int i = 0; i < p.nslots; ++i) {
-    p.slot[i] = take(rows * s.H * s.elem);
-    p.slot_act[i] = take(rows * s.I * s.elem);
-  }
+  for (int i = 0; i < p.nslots; ++i) p.slot[i] = take(rows * s.H * s.elem);
+  // act of both slots back to back: a fused pair uses it as one [2 rows][I] buffer
+  const size_t act = take(p.nslots * rows * s.I * s.elem);
+  for (int i = 0; i < p.nslots; ++i) p.slot_act[i] = act + i * rows * s.I * s.elem;
   p.bytes = o;
   return p;
 }
 
-// Two events per device, cached per host thread (used only to order s0/s1).
-struct EventPair {
+// Events that order s0 and s1, per device, cached per host thread.  A wait
+// refers to the event's latest record at the time of the wait call, so one
+// event can be recorded again for every pair.
+constexpr int kEvents = 3;
+struct DeviceEvents {
   int device = -1;
-  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipEvent_t ev[kEvents] = {};
 };
 
-hipError_t thread_events(hipEvent_t* meta_done, hipEvent_t* s1_done) {
-  thread_local std::vector<EventPair> cache;
+hipError_t thread_events(hipEvent_t (&out)[kEvents]) {
+  thread_local std::vector<DeviceEvents> cache;
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   for (auto& p : cache)
     if (p.device == dev) {
-      *meta_done = p.ev[0];
-      *s1_done = p.ev[1];
+      for (int i = 0; i < kEvents; ++i) out[i] = p.ev[i];
       return hipSuccess;
     }
-  EventPair p;
+  DeviceEvents p;
   p.device = dev;
   for (auto& e : p.ev) {
     err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
     if (err != hipSuccess) return err;
   }
   cache.push_back(p);
-  *meta_done = p.ev[0];
-  *s1_done = p.ev[1];
+  for (int i = 0; i < kEvents; ++i) out[i] = p.ev[i];
   return hipSuccess;
+}
+
+// s_to waits for all work enqueued so far on s_from.
+hipError_t join(hipStream_t s_to, hipStream_t s_from, hipEvent_t ev) {
+  hipError_t he = hipEventRecord(ev, s_from);
+  if (he == hipSuccess) he = hipStreamWaitEvent(s_to, ev, 0);
+  return he;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -89,16 +97,50 @@ moe_status check_chunk(const Shape& s, int chunk, int* t0, int* t1) {
   return MOE_OK;
 }
 
-moe_status gate_up(const Shape& s, int64_t rows, const void* x, const int32_t* off,
-                   const void* w, void* act, hipStream_t st) {
-  return hip_status(s.dtype == MOE_BF16 ? launch_gate_up_bf16(s, rows, x, off, w, act, st)
-                                        : launch_gate_up_f32(s, rows, x, off, w, act, st));
+moe_status gate_up(const Shape& s, const GroupedIO& io, const void* w, hipStream_t st) {
+  return hip_status(s.dtype == MOE_BF16 ? launch_gate_up_bf16(s, io, w, st)
+                                        : launch_gate_up_f32(s, io, w, st));
 }
 
-moe_status down(const Shape& s, int64_t rows, const void* act, const int32_t* off,
-                const void* w, void* y, hipStream_t st) {
-  return hip_status(s.dtype == MOE_BF16 ? launch_down_bf16(s, rows, act, off, w, y, st)
-                                        : launch_down_f32(s, rows, act, off, w, y, st));
+moe_status down(const Shape& s, const GroupedIO& io, const void* w, hipStream_t st) {
+  return hip_status(s.dtype == MOE_BF16 ? launch_down_bf16(s, io, w, st)
+                                        : launch_down_f32(s, io, w, st));
+}
+
+// One chunk: A and C are the chunk's own buffers.
+GroupedIO single(const Shape& s, int64_t rows, const void* a, const int32_t* off_c, void* c) {
+  GroupedIO io{};
+  io.a[0] = a;
+  io.c[0] = c;
+  io.off[0] = off_c;
+  io.rows_bound = rows;
+  (void)s;
+  return io;
+}
+
+// gate_up then down over both chunks of a pair (or one chunk when rows1 == 0):
+// x_perm and y split over the two slots, act joint.
+moe_status pair_ffn(const Shape& s, const int32_t* off0, const int32_t* off1, int64_t rows0,
+                    int64_t rows1, const void* x0, const void* x1, const void* w_gate_up,
+                    const void* w_down, void* act, void* y0, void* y1, hipStream_t st) {
+  GroupedIO io{};
+  io.off[0] = off0;
+  io.off[1] = rows1 > 0 ? off1 : nullptr;
+  io.rows_bound = rows0 + rows1;
+  io.a[0] = x0;
+  io.a[1] = x1;
+  io.a_split = true;
+  io.c[0] = act;
+  io.c_split = false;
+  moe_status r = gate_up(s, io, w_gate_up, st);
+  if (r != MOE_OK) return r;
+  io.a[0] = act;
+  io.a[1] = nullptr;
+  io.a_split = false;
+  io.c[0] = y0;
+  io.c[1] = y1;
+  io.c_split = true;
+  return down(s, io, w_down, st);
 }
 
 }  // namespace
@@ -237,8 +279,9 @@ moe_status moe_expert_gate_up(const moe_shape* shape, int32_t chunk, const void*
   if (!aligned(x_perm, 16) || !aligned(w_gate_up, 16) || !aligned(act, 16) ||
       !aligned(offsets, 4))
     return MOE_ERR_INVALID_ARG;
-  return gate_up(s, (int64_t)(t1 - t0) * s.k, x_perm, offsets + (size_t)chunk * (s.E + 1),
-                 w_gate_up, act, stream);
+  return gate_up(s, single(s, (int64_t)(t1 - t0) * s.k, x_perm,
+                           offsets + (size_t)chunk * (s.E + 1), act),
+                 w_gate_up, stream);
 }
 
 moe_status moe_expert_down(const moe_shape* shape, int32_t chunk, const void* act,
@@ -253,8 +296,8 @@ moe_status moe_expert_down(const moe_shape* shape, int32_t chunk, const void* ac
   if (!act || !offsets || !w_down || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned(act, 16) || !aligned(w_down, 16) || !aligned(y, 16) || !aligned(offsets, 4))
     return MOE_ERR_INVALID_ARG;
-  return down(s, (int64_t)(t1 - t0) * s.k, act, offsets + (size_t)chunk * (s.E + 1), w_down, y,
-              stream);
+  return down(s, single(s, (int64_t)(t1 - t0) * s.k, act, offsets + (size_t)chunk * (s.E + 1), y),
+              w_down, stream);
 }
 
 moe_status moe_expert_ffn(const moe_shape* shape, int32_t chunk, const void* x_perm,
@@ -263,6 +306,93 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t chunk, const void* x_p
   moe_status st = moe_expert_gate_up(shape, chunk, x_perm, offsets, w_gate_up, act, stream);
   if (st != MOE_OK) return st;
   return moe_expert_down(shape, chunk, act, offsets, w_down, y, stream);
+}
+
+namespace moe {
+namespace {
+
+// Checks shared by the pair entry points; fills the pair's offsets and row counts.
+moe_status pair_args(const moe_shape* shape, int32_t chunk, Shape* s, const int32_t* offsets,
+                     const int32_t** off0, const int32_t** off1, int64_t* rows0,
+                     int64_t* rows1) {
+  int t0, t1, u0 = 0, u1 = 0;
+  moe_status st = resolve_shape(shape, s);
+  if (st == MOE_OK) st = check_chunk(*s, chunk, &t0, &t1);
+  if (st != MOE_OK) return st;
+  if (chunk + 1 < s->N) chunk_tokens(*s, chunk + 1, &u0, &u1);
+  *rows0 = (int64_t)(t1 - t0) * s->k;
+  *rows1 = (int64_t)(u1 - u0) * s->k;
+  if (*rows0 + *rows1 == 0) return MOE_OK;
+  if (!offsets || !aligned(offsets, 4)) return MOE_ERR_INVALID_ARG;
+  *off0 = offsets + (size_t)chunk * (s->E + 1);
+  *off1 = *rows1 > 0 ? *off0 + (s->E + 1) : nullptr;
+  return MOE_OK;
+}
+
+// A chunk buffer: required and 16-byte aligned when its chunk has rows.
+bool buf_ok(const void* p, int64_t rows) { return rows == 0 || (p && aligned(p, 16)); }
+
+}  // namespace
+}  // namespace moe
+
+moe_status moe_expert_gate_up_pair(const moe_shape* shape, int32_t chunk, const void* x_perm0,
+                                   const void* x_perm1, const int32_t* offsets,
+                                   const void* w_gate_up, void* act, hipStream_t stream) {
+  Shape s;
+  const int32_t *off0 = nullptr, *off1 = nullptr;
+  int64_t rows0 = 0, rows1 = 0;
+  moe_status st = pair_args(shape, chunk, &s, offsets, &off0, &off1, &rows0, &rows1);
+  if (st != MOE_OK || rows0 + rows1 == 0) return st;
+  if (!buf_ok(x_perm0, rows0) || !buf_ok(x_perm1, rows1) || !buf_ok(act, 1) ||
+      !buf_ok(w_gate_up, 1))
+    return MOE_ERR_INVALID_ARG;
+  GroupedIO io{};
+  io.off[0] = off0;
+  io.off[1] = off1;
+  io.rows_bound = rows0 + rows1;
+  io.a[0] = x_perm0;
+  io.a[1] = x_perm1;
+  io.a_split = true;
+  io.c[0] = act;
+  return gate_up(s, io, w_gate_up, stream);
+}
+
+moe_status moe_expert_down_pair(const moe_shape* shape, int32_t chunk, const void* act,
+                                const int32_t* offsets, const void* w_down, void* y0, void* y1,
+                                hipStream_t stream) {
+  Shape s;
+  const int32_t *off0 = nullptr, *off1 = nullptr;
+  int64_t rows0 = 0, rows1 = 0;
+  moe_status st = pair_args(shape, chunk, &s, offsets, &off0, &off1, &rows0, &rows1);
+  if (st != MOE_OK || rows0 + rows1 == 0) return st;
+  if (!buf_ok(y0, rows0) || !buf_ok(y1, rows1) || !buf_ok(act, 1) || !buf_ok(w_down, 1))
+    return MOE_ERR_INVALID_ARG;
+  GroupedIO io{};
+  io.off[0] = off0;
+  io.off[1] = off1;
+  io.rows_bound = rows0 + rows1;
+  io.a[0] = act;
+  io.c[0] = y0;
+  io.c[1] = y1;
+  io.c_split = true;
+  return down(s, io, w_down, stream);
+}
+
+moe_status moe_expert_ffn_pair(const moe_shape* shape, int32_t chunk, const void* x_perm0,
+                               const void* x_perm1, const int32_t* offsets,
+                               const void* w_gate_up, const void* w_down, void* act, void* y0,
+                               void* y1, hipStream_t stream) {
+  Shape s;
+  const int32_t *off0 = nullptr, *off1 = nullptr;
+  int64_t rows0 = 0, rows1 = 0;
+  moe_status st = pair_args(shape, chunk, &s, offsets, &off0, &off1, &rows0, &rows1);
+  if (st != MOE_OK || rows0 + rows1 == 0) return st;
+  // every argument of both launches is checked before the first is enqueued
+  if (!buf_ok(x_perm0, rows0) || !buf_ok(x_perm1, rows1) || !buf_ok(y0, rows0) ||
+      !buf_ok(y1, rows1) || !buf_ok(act, 1) || !buf_ok(w_gate_up, 1) || !buf_ok(w_down, 1))
+    return MOE_ERR_INVALID_ARG;
+  return pair_ffn(s, off0, off1, rows0, rows1, x_perm0, x_perm1, w_gate_up, w_down, act, y0, y1,
+                  stream);
 }
 
 moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const void* y,
@@ -280,14 +410,16 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
   return hip_status(launch_combine(s, t0, t1, y, dst_row, top_k_weights, out, stream));
 }
 
-moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states,
-                               const int32_t* top_k_index, const float* top_k_weights,
-                               const void* w_gate_up, const void* w_down, void* out,
-                               int32_t* dev_error, void* ws, size_t ws_bytes, hipStream_t s0,
-                               hipStream_t s1) {
+moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidden_states,
+                                        const int32_t* top_k_index, const float* top_k_weights,
+                                        const void* w_gate_up, const void* w_down, void* out,
+                                        int32_t* dev_error, void* ws, size_t ws_bytes,
+                                        hipStream_t s0, hipStream_t s1, int32_t schedule) {
   Shape s;
   moe_status st = resolve_shape(shape, &s);
   if (st != MOE_OK) return st;
+  if (schedule != MOE_SCHEDULE_PAIR_FUSED && schedule != MOE_SCHEDULE_PER_CHUNK)
+    return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   if (!aligned(dev_error, 4)) return MOE_ERR_INVALID_ARG;
   const FwdPlan p = fwd_plan(s);
@@ -314,40 +446,89 @@ moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states
   if (s.T == 0) return MOE_OK;
 
   const bool two = (s1 != nullptr && s1 != s0 && s.N >= 2);
-  hipEvent_t meta_done = nullptr, s1_done = nullptr;
+  hipEvent_t ev[kEvents] = {};
   if (two) {
-    he = thread_events(&meta_done, &s1_done);
-    if (he == hipSuccess) he = hipEventRecord(meta_done, s0);
-    if (he == hipSuccess) he = hipStreamWaitEvent(s1, meta_done, 0);
+    he = thread_events(ev);
+    if (he == hipSuccess) he = join(s1, s0, ev[0]);  // s1 starts after the metadata
     if (he != hipSuccess) return MOE_ERR_HIP;
   }
   bool used_s1 = false;
-  for (int c = 0; c < s.N; ++c) {
-    int t0, t1;
-    chunk_tokens(s, c, &t0, &t1);
-    if (t1 == t0) continue;  // empty tail chunk: no rows, nothing to launch
-    const int slot = c % p.nslots;
-    hipStream_t st_c = (two && (c & 1)) ? s1 : s0;
-    used_s1 |= (st_c == s1 && two);
-    void* xy = w + p.slot[slot];
-    void* act = w + p.slot_act[slot];
-    const int64_t rows = (int64_t)(t1 - t0) * s.k;
-    const int32_t* off_c = offsets + (size_t)c * (s.E + 1);
-    he = launch_permute(s, t0, t1, hidden_states, dst_row, xy, st_c);
-    if (he != hipSuccess) return MOE_ERR_HIP;
-    st = gate_up(s, rows, xy, off_c, w_gate_up, act, st_c);
-    if (st != MOE_OK) return st;
-    st = down(s, rows, act, off_c, w_down, xy, st_c);  // y overwrites the dead x_perm
-    if (st != MOE_OK) return st;
-    he = launch_combine(s, t0, t1, xy, dst_row, top_k_weights, out, st_c);
-    if (he != hipSuccess) return MOE_ERR_HIP;
+  auto chunk_rows = [&](int c, int* t0, int* t1) {
+    *t0 = *t1 = 0;
+    if (c < s.N) chunk_tokens(s, c, t0, t1);
+    return (int64_t)(*t1 - *t0) * s.k;
+  };
+
+  if (schedule == MOE_SCHEDULE_PAIR_FUSED) {
+    // Pair (c, c+1): both permutes (c on s0, c+1 on s1), then one gate_up and
+    // one down launch over the pair's rows on s0, then both combines (c on s0,
+    // c+1 on s1).  Every expert's weights are streamed once per pair.
+    for (int c = 0; c < s.N; c += 2) {
+      int t0, t1, u0, u1;
+      const int64_t rows0 = chunk_rows(c, &t0, &t1), rows1 = chunk_rows(c + 1, &u0, &u1);
+      if (rows0 + rows1 == 0) continue;  // empty tail pair
+      hipStream_t st1 = two ? s1 : s0;
+      void* xy0 = w + p.slot[0];
+      void* xy1 = p.nslots > 1 ? w + p.slot[1] : nullptr;
+      he = launch_permute(s, t0, t1, hidden_states, dst_row, xy0, s0);
+      if (he == hipSuccess && rows1 > 0)
+        he = launch_permute(s, u0, u1, hidden_states, dst_row, xy1, st1);
+      if (he == hipSuccess && two && rows1 > 0) {
+        used_s1 = true;
+        he = join(s0, s1, ev[1]);
+      }
+      if (he != hipSuccess) return MOE_ERR_HIP;
+      const int32_t* off0 = offsets + (size_t)c * (s.E + 1);
+      // y overwrites the dead x_perm of each slot
+      st = pair_ffn(s, off0, off0 + (s.E + 1), rows0, rows1, xy0, xy1, w_gate_up, w_down,
+                    w + p.slot_act[0], xy0, xy1, s0);
+      if (st != MOE_OK) return st;
+      if (two && rows1 > 0) {
+        he = join(s1, s0, ev[2]);
+        if (he != hipSuccess) return MOE_ERR_HIP;
+      }
+      he = launch_combine(s, t0, t1, xy0, dst_row, top_k_weights, out, s0);
+      if (he == hipSuccess && rows1 > 0)
+        he = launch_combine(s, u0, u1, xy1, dst_row, top_k_weights, out, st1);
+      if (he != hipSuccess) return MOE_ERR_HIP;
+    }
+  } else {
+    // Chunk c: permute -> gate_up -> down -> combine on stream s[c % 2], slot c % 2.
+    for (int c = 0; c < s.N; ++c) {
+      int t0, t1;
+      const int64_t rows = chunk_rows(c, &t0, &t1);
+      if (rows == 0) continue;  // empty tail chunk: nothing to launch
+      const int slot = c % p.nslots;
+      hipStream_t st_c = (two && (c & 1)) ? s1 : s0;
+      used_s1 |= (st_c == s1 && two);
+      void* xy = w + p.slot[slot];
+      void* act = w + p.slot_act[slot];
+      const int32_t* off_c = offsets + (size_t)c * (s.E + 1);
+      he = launch_permute(s, t0, t1, hidden_states, dst_row, xy, st_c);
+      if (he != hipSuccess) return MOE_ERR_HIP;
+      st = gate_up(s, single(s, rows, xy, off_c, act), w_gate_up, st_c);
+      if (st != MOE_OK) return st;
+      st = down(s, single(s, rows, act, off_c, xy), w_down, st_c);  // y overwrites x_perm
+      if (st != MOE_OK) return st;
+      he = launch_combine(s, t0, t1, xy, dst_row, top_k_weights, out, st_c);
+      if (he != hipSuccess) return MOE_ERR_HIP;
+    }
   }
   if (two && used_s1) {
-    he = hipEventRecord(s1_done, s1);
-    if (he == hipSuccess) he = hipStreamWaitEvent(s0, s1_done, 0);
+    he = join(s0, s1, ev[1]);
     if (he != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states,
+                               const int32_t* top_k_index, const float* top_k_weights,
+                               const void* w_gate_up, const void* w_down, void* out,
+                               int32_t* dev_error, void* ws, size_t ws_bytes, hipStream_t s0,
+                               hipStream_t s1) {
+  return moe_chunked_forward_schedule(shape, hidden_states, top_k_index, top_k_weights,
+                                      w_gate_up, w_down, out, dev_error, ws, ws_bytes, s0, s1,
+                                      MOE_SCHEDULE_PAIR_FUSED);
 }
 
 }  // extern "C"

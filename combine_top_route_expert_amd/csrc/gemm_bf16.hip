@@ -1,4 +1,4 @@
-// Grouped expert GEMMs on gfx950 bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+// Grouped expert GEMMs on gfx950 bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // The expert computation of the MindSpeed Chunk MoE article (core principle /
 // timing-diagram sections) is read as a SwiGLU FFN per expert; each expert
@@ -15,28 +15,38 @@
 // vmcnt waits plus a plain s_barrier (no fence that would drain every load).
 // Inside a 1 KB block lane l holds row l/8 and 16-byte slot l%8; the global
 // chunk it fetches is slot ^ ((row >> 1) & 7), which makes the 16-byte fragment
-// reads of 16 consecutive rows hit distinct LDS banks.
+// reads of 16 consecutive rows hit distinct LDS banks (measured: no bank
+// conflicts).
+//
+// Matrix instruction: on gfx950 v_mfma_f32_32x32x16_bf16 and
+// v_mfma_f32_16x16x32_bf16 both occupy the matrix pipe for about 32 cycles, so
+// only the 32x32x16 form reaches the chip's dense bf16 peak (measured 2.47
+// versus 1.26 PFLOP/s with back-to-back independent MFMAs); every tile here is
+// built from 32 x 32 blocks.
 //
 // Tiling: a workgroup computes BM x BN with WAVES_M x WAVES_N waves; each wave
-// owns (BM/WAVES_M) x (BN/WAVES_N) as 16 x 16 MFMA blocks with fp32
+// owns (BM/WAVES_M) x (BN/WAVES_N) as 32 x 32 MFMA blocks with fp32
 // accumulators.  For gate_up half of every wave's columns are gate columns and
 // the other half the matching up columns, so each lane holds the gate and up
 // accumulators of the same (row, i) and SwiGLU runs in registers: no
 // [rows][2I] intermediate is written.
 //
 // Grouping: m-tiles of all experts are numbered expert by expert; every
-// workgroup finds its expert from the device-resident offsets (find_m_tile),
-// so the host never reads group sizes.  The grid is bounded from the chunk's
-// assignment count and surplus workgroups exit.  Rows past an expert's block
+// workgroup builds that numbering from the device-resident offsets (MTileMap),
+// so the host never reads group sizes.  Each XCD takes a contiguous range of
+// m-tiles with all their n-tiles (xcd_tile), keeping activation and weight
+// panels in one L2.  The grid is bounded from the chunk's assignment count and
+// surplus workgroups exit.  Rows past an expert's block
 // are loaded from a clamped row and never stored.  Two workgroups per CU (or
 // eight waves in one) let one wave's barrier and LDS-read bubbles hide behind
 // another's MFMAs; a persistent variant with deeper prefetch measured slower.
 //
-// Instances: a wide 256 x 256 tile with 8 waves for experts with many rows, a
-// 128 x 128 tile (two workgroups per CU) for medium blocks and a 64 x 128 tile
-// for decode-sized blocks, picked from the average rows per expert.  All use
-// the same MFMA instruction and the same order of K steps, so a row gets the
-// same bits from any instance or chunking.
+// Instances: a 256 x 256 tile with 8 waves for large GEMMs with long expert
+// blocks or long K / N, a 64 x 128 tile (three workgroups per CU) otherwise.
+// All use the same MFMA instruction and the same order of K steps, so a row
+// gets the same bits from any instance or chunking.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -44,232 +54,332 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int BK = 64;             // K elements per stage
-constexpr int ROW_BYTES = BK * 2;  // bytes of one tile row per stage
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14])
 constexpr int wait_vm(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
 struct GemmArgs {
-  const uint16_t* A;          // [rows][K] bf16
+  const uint16_t* A[2];       // [rows][K] bf16 (A[1]: chunk-1 rows when a_split)
   const uint16_t* B;          // [E][b_rows][K] bf16
-  uint16_t* C;                // [rows][ncols] bf16
-  const int32_t* off;         // E + 1 offsets of this chunk
+  uint16_t* C[2];             // [rows][ncols] bf16 (C[1]: chunk-1 rows when c_split)
+  const int32_t* off0;        // E + 1 offsets of the (first) chunk
+  const int32_t* off1;        // E + 1 offsets of the pair's second chunk, or null
+  int a_split, c_split;
   int E, K, I, ncols, n_tiles;
+  int lo_rows, hi_rows;       // experts handled by this launch: lo_rows <= rows < hi_rows
   int64_t b_expert_stride;    // elements per expert in B
 };
+
+// Address of virtual row v of the tile's expert on one side of the product.
+__device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* const (&base)[2], int split,
+                                                   const TileRows& tr, int v, int64_t ld) {
+  if (split) {
+    int part;
+    const int r = tr.split_row(v, &part);
+    return (part ? base[1] : base[0]) + (int64_t)r * ld;
+  }
+  return base[0] + (int64_t)tr.joint_row(v) * ld;
+}
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-template <bool kGateUp, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(GemmArgs a) {
-  constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int LA = BM / 8 / NW, LB = BN / 8 / NW;  // 1 KB loads per wave per stage
-  constexpr int STAGE_BYTES = (BM + BN) * ROW_BYTES;
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows per wave");
-  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
-  static_assert(!kGateUp || WN % 32 == 0, "gate/up halves");
-  static_assert(STAGES >= 2, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+// LDS layout of one stage: BM rows of A then BN rows of B, each row BK bf16
+// (ROW_BYTES) holding CH 16-byte chunks; chunk c of row r sits at slot
+// c ^ swz(r).  A 16-lane phase of a 16-byte fragment read covers 16
+// consecutive rows at one chunk; rows r and r + RB share a position in a
+// 256-byte bank line, so swz(r) = (r / RB) mod CH spreads the 16 rows over 16
+// distinct 16-byte bank groups (measured: no bank conflicts).
+template <int BK>
+struct StageGeom {
+  static constexpr int ROW_BYTES = BK * 2;
+  static constexpr int CH = BK / 8;               // 16-byte chunks per row
+  static constexpr int RPB = 1024 / ROW_BYTES;     // rows per 1 KB direct-to-LDS block
+  static constexpr int RB = 256 / ROW_BYTES;       // rows per 256-byte bank line
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static __device__ __forceinline__ int swz(int r) { return (r / RB) & (CH - 1); }
+  // 32x32x16 fragment of a 32-row block: lane l holds row l % 32 and the eight
+  // K elements of 16-byte chunk 2*kk + l/32 of the stage.
+  static __device__ __forceinline__ int frag_offset(int lane, int kk) {
+    const int r = lane & 31;
+    const int chunk = 2 * kk + (lane >> 5);
+    return r * ROW_BYTES + ((chunk ^ swz(r)) << 4);
+  }
+};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int nt = blockIdx.x % a.n_tiles;
-  const int mt = blockIdx.x / a.n_tiles;
-  int e, m0, mrows;
-  if (!find_m_tile(a.off, a.E, BM, mt, &e, &m0, &mrows)) return;
-
-  // Per-lane source of every direct-to-LDS load (at k = 0).
-  const int brow_in_blk = lane >> 3, slot = lane & 7;
+// Everything a workgroup needs to stream its tile's A and B stages into LDS.
+template <bool kGateUp, int BM, int BN, int NW, int WN, int BK>
+struct TileLoader {
+  using G = StageGeom<BK>;
+  static constexpr int LA = BM / G::RPB / NW, LB = BN / G::RPB / NW;  // 1 KB loads per wave
+  static constexpr int STAGE_BYTES = (BM + BN) * G::ROW_BYTES;
+  static_assert(LA * G::RPB * NW == BM && LB * G::RPB * NW == BN, "tile rows per wave");
   const char* a_src[LA];
   const char* b_src[LB];
+  int wave, mrows;
+  int live_a;  // A blocks of this wave that hold rows of the tile (the rest are skipped)
+
+  __device__ __forceinline__ void init(const GemmArgs& a, const TileRows& tr, int nt, int lane,
+                                       int wave_) {
+    wave = wave_;
+    mrows = tr.rows;
+    const int row_in_blk = lane / G::CH, slot = lane % G::CH;
+    live_a = 0;
 #pragma unroll
-  for (int t = 0; t < LA; ++t) {
-    const int row = (wave * LA + t) * 8 + brow_in_blk;
-    const int chunk = slot ^ ((row >> 1) & 7);
-    const int r = row < mrows ? row : mrows - 1;
-    a_src[t] = (const char*)(a.A + (int64_t)(m0 + r) * a.K + chunk * 8);
-  }
-  const uint16_t* Be = a.B + (int64_t)e * a.b_expert_stride;
-#pragma unroll
-  for (int t = 0; t < LB; ++t) {
-    const int col = (wave * LB + t) * 8 + brow_in_blk;  // tile column = B row
-    const int chunk = slot ^ ((col >> 1) & 7);
-    int brow;
-    if constexpr (kGateUp) {
-      const int cw = col / WN, w = col % WN;
-      const int q = w / (WN / 2), c = w % (WN / 2);
-      brow = q * a.I + nt * (BN / 2) + cw * (WN / 2) + c;
-    } else {
-      brow = nt * BN + col;
-      if (brow > a.ncols - 1) brow = a.ncols - 1;
+    for (int t = 0; t < LA; ++t) {
+      const int row = (wave * LA + t) * G::RPB + row_in_blk;
+      const int chunk = slot ^ G::swz(row);
+      const int r = row < mrows ? row : mrows - 1;
+      a_src[t] = (const char*)(row_ptr(a.A, a.a_split, tr, tr.v0 + r, a.K) + chunk * 8);
+      live_a += (wave * LA + t) * G::RPB < mrows ? 1 : 0;
     }
-    b_src[t] = (const char*)(Be + (int64_t)brow * a.K + chunk * 8);
+    const int e = tr.e;
+    const uint16_t* Be = a.B + (int64_t)e * a.b_expert_stride;
+#pragma unroll
+    for (int t = 0; t < LB; ++t) {
+      const int col = (wave * LB + t) * G::RPB + row_in_blk;  // tile column = B row
+      const int chunk = slot ^ G::swz(col);
+      int brow;
+      if constexpr (kGateUp) {
+        // each wave's WN columns: gate for the first half, the matching up rows after
+        const int cw = col / WN, w = col % WN;
+        const int q = w / (WN / 2), c = w % (WN / 2);
+        brow = q * a.I + nt * (BN / 2) + cw * (WN / 2) + c;
+      } else {
+        brow = nt * BN + col;
+        if (brow > a.ncols - 1) brow = a.ncols - 1;
+      }
+      b_src[t] = (const char*)(Be + (int64_t)brow * a.K + chunk * 8);
+    }
   }
 
-  auto issue = [&](int kt, int buf) {
+  // Loads one stage.  A blocks of 1 KB that lie wholly past the tile's rows are
+  // not loaded (their LDS rows feed only outputs that are never stored), so a
+  // wave issues live_a + LB loads per stage.
+  __device__ __forceinline__ void issue(char* smem, int kt, int buf) const {
     char* base = smem + buf * STAGE_BYTES;
-    const int64_t koff = (int64_t)kt * ROW_BYTES;
+    const int64_t koff = (int64_t)kt * G::ROW_BYTES;
 #pragma unroll
     for (int t = 0; t < LA; ++t)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff),
-                                       (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+      if (t < live_a)
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff),
+                                         (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
 #pragma unroll
     for (int t = 0; t < LB; ++t)
       __builtin_amdgcn_global_load_lds(
           (const void*)(b_src[t] + koff),
-          (lds_void*)(base + BM * ROW_BYTES + (wave * LB + t) * 1024), 16, 0, 0);
-  };
+          (lds_void*)(base + BM * G::ROW_BYTES + (wave * LB + t) * 1024), 16, 0, 0);
+  }
+};
 
-  f32x4 acc[FM][FN];
+// Waits until at most n of this wave's vector memory operations are pending
+// (s_waitcnt takes an immediate, so n is dispatched over its possible values).
+__device__ __forceinline__ void wait_loads(int n) {
+#define MOE_WAIT_CASE(v)                    \
+  case v:                                   \
+    __builtin_amdgcn_s_waitcnt(wait_vm(v)); \
+    return;
+  switch (n) {
+    MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+    MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
+    MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14) MOE_WAIT_CASE(15)
+    MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18) MOE_WAIT_CASE(19) MOE_WAIT_CASE(20)
+    MOE_WAIT_CASE(21) MOE_WAIT_CASE(22) MOE_WAIT_CASE(23) MOE_WAIT_CASE(24)
+    default:  // n <= 0, or beyond the table: wait for every load
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      return;
+  }
+#undef MOE_WAIT_CASE
+}
+
+// Epilogue for one wave's FM x FN blocks.  MFMA 32x32 output: lane l holds
+// column l % 32 of rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of each block.
+template <bool kGateUp, int FM, int FN, int BN, int WM, int WN>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
+                                           const TileRows& tr, int nt, int wm, int wn, int lane) {
+  const int rbase = wm * WM + 4 * (lane >> 5);
+  const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < 16; ++q) {
+      const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+      if (row >= tr.rows) continue;
+      uint16_t* crow = (uint16_t*)row_ptr(cbase, a.c_split, tr, tr.v0 + row, a.ncols);
+      if constexpr (kGateUp) {
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int col = nt * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
+          const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
+          crow[col] = to_bf16_bits(g / (1.0f + expf(-g)) * u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
+          if (col < a.ncols) crow[col] = to_bf16_bits(acc[i][j][q]);
+        }
+      }
+    }
+}
 
-  // fragment read offset: row (lane & 15), 16-byte chunk (lane >> 4) (+4 for k 32..63)
-  const int frag0 = (lane & 15) * ROW_BYTES + (((lane >> 4) ^ ((lane & 15) >> 1)) << 4);
+template <bool kGateUp, int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(GemmArgs a) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  using Loader = TileLoader<kGateUp, BM, BN, NW, WN, BK>;
+  using G = StageGeom<BK>;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(!kGateUp || WN % 64 == 0, "gate/up halves");
+  static_assert(STAGES >= 2, "pipeline depth");
+  static_assert((STAGES - 2) * (Loader::LA + Loader::LB) <= 24, "wait_loads range");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * Loader::STAGE_BYTES];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  MTileMap tm;
+  tm.build(a.off0, a.off1, a.E, BM, a.lo_rows, a.hi_rows);
+  int mt, nt;
+  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
+  Loader ld;
+  ld.init(a, tr, nt, lane, wave);
+  const int per_stage = ld.live_a + Loader::LB;  // loads this wave issues per stage
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
   const int KT = a.K / BK;
+  // a wave whose rows all lie past the tile's rows has no MFMA work
+  const bool rows_live = wm * WM < tr.rows;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) issue(s, s);
+    if (s < KT) ld.issue(smem, s, s);
 
   for (int kt = 0; kt < KT; ++kt) {
-    // stage kt has landed once at most STAGES-2 newer stages are still in flight
-    if (kt + STAGES - 2 < KT)
-      __builtin_amdgcn_s_waitcnt(wait_vm((LA + LB) * (STAGES - 2)));
-    else
-      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    // stage kt has landed once only the newer stages issued so far are pending
+    const int newer = KT - 1 - kt < STAGES - 2 ? KT - 1 - kt : STAGES - 2;
+    wait_loads(newer * per_stage);
     __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const char* sa = smem + (kt % STAGES) * STAGE_BYTES;
-    const char* sb = sa + BM * ROW_BYTES;
+    if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const char* sa = smem + (kt % STAGES) * Loader::STAGE_BYTES;
+    const char* sb = sa + BM * G::ROW_BYTES;
+    if (rows_live) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int fo = kk ? (frag0 ^ 64) : frag0;
-      bf16x8 af[FM], bfr[FN];
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int fo = G::frag_offset(lane, kk);
+        bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8*)(sa + (wm * WM + i * 16) * ROW_BYTES + fo);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 16) * ROW_BYTES + fo);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
+          af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * G::ROW_BYTES + fo);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
     }
     // this stage's LDS reads are complete before any wave refills its buffer
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
-
-  // Epilogue.  MFMA 16x16 output: lane holds column (lane & 15) of rows
-  // 4 * (lane >> 4) + 0..3 of each 16 x 16 block.
-  const int rbase = wm * WM + (lane >> 4) * 4;
-  if constexpr (kGateUp) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN / 2; ++j) {
-        const int col = nt * (BN / 2) + wn * (WN / 2) + j * 16 + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + i * 16 + r;
-          if (row < mrows) {
-            const float g = acc[i][j][r], u = acc[i][j + FN / 2][r];
-            const float act = g / (1.0f + expf(-g)) * u;
-            a.C[(int64_t)(m0 + row) * a.ncols + col] = to_bf16_bits(act);
-          }
-        }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = nt * BN + wn * WN + j * 16 + (lane & 15);
-        if (col >= a.ncols) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = rbase + i * 16 + r;
-          if (row < mrows) a.C[(int64_t)(m0 + row) * a.ncols + col] = to_bf16_bits(acc[i][j][r]);
-        }
-      }
-  }
+  store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
 }
 
 // Tile instances.  All use the same MFMA instruction and the same order of
 // K steps, so any instance gives the same bits for a row; the choice only
-// affects speed.
-enum Instance { kWide = 1, kMid = 2, kNarrow = 3 };
+// affects speed.  A compile-time override forces one instance, for
+// comparisons.
+enum Instance {
+  kAuto = 0,
+  kWide64x2 = 1,    // 256 x 256, 8 waves, BK 64, 2 stages (128 KB LDS)
+  kWide32x4 = 2,    // 256 x 256, 8 waves, BK 32, 4 stages (128 KB LDS)
+  kWide32x5 = 3,    // 256 x 256, 8 waves, BK 32, 5 stages (160 KB LDS)
+  kTall64x3 = 4,    // 256 x 128, 8 waves, BK 64, 3 stages (144 KB LDS)
+  kNarrow64x2 = 5,  // 64 x 128, 4 waves, BK 64, 2 stages (48 KB LDS, 3 per CU)
+  kNarrow32x4 = 6,  // 64 x 128, 4 waves, BK 32, 4 stages (48 KB LDS, 3 per CU)
+  kMid32x4 = 7,     // 128 x 128, 4 waves, BK 32, 4 stages (64 KB LDS, 2 per CU)
+};
 #ifndef MOE_GEMM_FORCE
 #define MOE_GEMM_FORCE 0
 #endif
-#ifndef MOE_GEMM_MID_STAGES
-#define MOE_GEMM_MID_STAGES 2
-#endif
 
-// Average rows per expert decides the tile: long blocks of rows amortise each
-// weight panel over a 256-row tile, short ones waste less of a 64-row tile.
-int choose_instance(int64_t rows_bound, int E) {
-  if (MOE_GEMM_FORCE) return MOE_GEMM_FORCE;
+bool prefer_wide(int64_t rows_bound, int E, int K, int ncols) {
   const int64_t avg = rows_bound / (E > 0 ? E : 1);
-  if (avg >= 512) return kWide;
-  if (avg >= 24) return kMid;
-  return kNarrow;
+  return rows_bound >= 4096 && (avg >= 192 || K >= 4096 || ncols >= 4096);
 }
 
-template <bool kGateUp, int BM, int BN, int WM_, int WN_, int ST>
-hipError_t launch_instance(const GemmArgs& a, int64_t rows_bound, int E, hipStream_t st) {
+template <bool kGateUp, int BM, int BN, int WM_, int WN_, int BK, int ST>
+hipError_t launch_instance(GemmArgs a, const Shape& s, int64_t rows_bound, hipStream_t st) {
   constexpr int threads = 64 * WM_ * WN_;
-  const int64_t grid = m_tiles_bound(rows_bound, E, BM) * a.n_tiles;
+  // gate_up tiles cover BN/2 intermediate columns (gate and up halves)
+  a.n_tiles = kGateUp ? s.I / (BN / 2) : (s.H + BN - 1) / BN;
+  a.lo_rows = 1;
+  a.hi_rows = 0x7fffffff;
+  const int64_t grid = xcd_grid(m_tiles_bound(rows_bound, s.E, BM), a.n_tiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((grouped_gemm_bf16<kGateUp, BM, BN, WM_, WN_, ST>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((grouped_gemm_bf16<kGateUp, BM, BN, WM_, WN_, BK, ST>), dim3((unsigned)grid),
                      dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool kGateUp>
 hipError_t launch_kind(int inst, GemmArgs a, const Shape& s, int64_t rows_bound, hipStream_t st) {
-  // n-tiles of the chosen instance; gate_up tiles cover BN/2 intermediate columns
-  auto ntiles = [&](int BN) {
-    return kGateUp ? s.I / (BN / 2) : (s.H + BN - 1) / BN;
-  };
-  if (kGateUp && inst == kWide && s.I % 128) inst = kMid;
+  // a 256-column gate_up tile holds 128 intermediate columns
+  const bool wide_ok = !kGateUp || s.I % 128 == 0;
+  if (inst == kAuto) {
+    const int ncols = kGateUp ? 2 * s.I : s.H;
+    inst = wide_ok && prefer_wide(rows_bound, s.E, a.K, ncols) ? kWide64x2 : kNarrow64x2;
+  }
+  if (!wide_ok && inst != kNarrow64x2 && inst != kNarrow32x4 && inst != kMid32x4)
+    inst = kNarrow64x2;
   switch (inst) {
-    case kWide:
-      a.n_tiles = ntiles(256);
-      return launch_instance<kGateUp, 256, 256, 2, 4, 2>(a, rows_bound, s.E, st);
-    case kNarrow:
-      a.n_tiles = ntiles(128);
-      return launch_instance<kGateUp, 64, 128, 1, 4, 4>(a, rows_bound, s.E, st);
+    case kWide64x2:
+      return launch_instance<kGateUp, 256, 256, 2, 4, 64, 2>(a, s, rows_bound, st);
+    case kWide32x4:
+      return launch_instance<kGateUp, 256, 256, 2, 4, 32, 4>(a, s, rows_bound, st);
+    case kWide32x5:
+      return launch_instance<kGateUp, 256, 256, 2, 4, 32, 5>(a, s, rows_bound, st);
+    case kTall64x3:
+      return launch_instance<kGateUp, 256, 128, 4, 2, 64, 3>(a, s, rows_bound, st);
+    case kNarrow32x4:
+      return launch_instance<kGateUp, 64, 128, 2, 2, 32, 4>(a, s, rows_bound, st);
+    case kMid32x4:
+      return launch_instance<kGateUp, 128, 128, 2, 2, 32, 4>(a, s, rows_bound, st);
     default:
-      a.n_tiles = ntiles(128);
-      return launch_instance<kGateUp, 128, 128, 2, 2, MOE_GEMM_MID_STAGES>(a, rows_bound, s.E, st);
+      return launch_instance<kGateUp, 64, 128, 2, 2, 64, 2>(a, s, rows_bound, st);
   }
 }
 
-hipError_t launch(bool gate_up, const Shape& s, int64_t rows_bound, const void* A,
-                  const int32_t* off, const void* B, void* C, hipStream_t st) {
+hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void* B,
+                  hipStream_t st) {
+  const int64_t rows_bound = io.rows_bound;
   if (rows_bound <= 0) return hipSuccess;
   GemmArgs a{};
-  a.A = (const uint16_t*)A;
+  a.A[0] = (const uint16_t*)io.a[0];
+  a.A[1] = (const uint16_t*)(io.a_split ? io.a[1] : io.a[0]);
+  a.C[0] = (uint16_t*)io.c[0];
+  a.C[1] = (uint16_t*)(io.c_split ? io.c[1] : io.c[0]);
+  a.off0 = io.off[0];
+  a.off1 = io.off[1];
+  a.a_split = io.a_split && io.off[1];
+  a.c_split = io.c_split && io.off[1];
   a.B = (const uint16_t*)B;
-  a.C = (uint16_t*)C;
-  a.off = off;
   a.E = s.E;
   a.I = s.I;
-  const int inst = choose_instance(rows_bound, s.E);
+  const int inst = MOE_GEMM_FORCE;
   if (gate_up) {
     a.K = s.H;
     a.ncols = s.I;
@@ -284,16 +394,14 @@ hipError_t launch(bool gate_up, const Shape& s, int64_t rows_bound, const void* 
 
 }  // namespace
 
-hipError_t launch_gate_up_bf16(const Shape& s, int64_t rows_bound, const void* x_perm,
-                               const int32_t* offsets_c, const void* w_gate_up, void* act,
+hipError_t launch_gate_up_bf16(const Shape& s, const GroupedIO& io, const void* w_gate_up,
                                hipStream_t st) {
-  return launch(true, s, rows_bound, x_perm, offsets_c, w_gate_up, act, st);
+  return launch(true, s, io, w_gate_up, st);
 }
 
-hipError_t launch_down_bf16(const Shape& s, int64_t rows_bound, const void* act,
-                            const int32_t* offsets_c, const void* w_down, void* y,
+hipError_t launch_down_bf16(const Shape& s, const GroupedIO& io, const void* w_down,
                             hipStream_t st) {
-  return launch(false, s, rows_bound, act, offsets_c, w_down, y, st);
+  return launch(false, s, io, w_down, st);
 }
 
 }  // namespace moe

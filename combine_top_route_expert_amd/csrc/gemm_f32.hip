@@ -1,7 +1,8 @@
 // Grouped expert GEMMs in fp32 (vector FMA), for dtype MOE_F32.
 //
-// Same contraction and grouping as the bf16 path (SwiGLU read of the expert
-// computation in the MindSpeed Chunk MoE article), in IEEE fp32 with one fused
+// Same contraction and grouping (one chunk, or the two chunks of a pair) as the
+// bf16 path (SwiGLU read of the expert computation in the MindSpeed Chunk MoE
+// article), in IEEE fp32 with one fused
 // multiply-add per product and ascending-k order inside each thread: no
 // reduced-precision matrix instruction is involved.
 //
@@ -19,13 +20,26 @@ constexpr int BM = 64, BN = 64, BK = 16;
 constexpr int kThreads = 256;
 
 struct GemmArgs {
-  const float* A;
+  const float* A[2];      // A[1]: chunk-1 rows when a_split
   const float* B;
-  float* C;
-  const int32_t* off;
+  float* C[2];            // C[1]: chunk-1 rows when c_split
+  const int32_t* off0;
+  const int32_t* off1;    // second chunk of a pair, or null
+  int a_split, c_split;
   int E, K, I, ncols, n_tiles;
   int64_t b_expert_stride;
 };
+
+// Address of virtual row v of the tile's expert on one side of the product.
+__device__ __forceinline__ const float* row_ptr(const float* const (&base)[2], int split,
+                                                const TileRows& tr, int v, int64_t ld) {
+  if (split) {
+    int part;
+    const int r = tr.split_row(v, &part);
+    return (part ? base[1] : base[0]) + (int64_t)r * ld;
+  }
+  return base[0] + (int64_t)tr.joint_row(v) * ld;
+}
 
 template <bool kGateUp>
 __device__ __forceinline__ int tile_col(int tx, int q) {
@@ -39,15 +53,17 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_f32(GemmArgs a) {
   __shared__ float As[BM][BK + 1];
   __shared__ float Bs[BN][BK + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int nt = blockIdx.x % a.n_tiles;
-  const int mt = blockIdx.x / a.n_tiles;
-  int e, m0, mrows;
-  if (!find_m_tile(a.off, a.E, BM, mt, &e, &m0, &mrows)) return;
+  MTileMap tm;
+  tm.build(a.off0, a.off1, a.E, BM);
+  int mt, nt;
+  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
+  const int e = tr.e, mrows = tr.rows;
 
   // one float4 of A and one of B per thread per stage
   const int lrow = tid >> 2, lk = (tid & 3) * 4;
   const int arow = lrow < mrows ? lrow : mrows - 1;
-  const float* a_src = a.A + (int64_t)(m0 + arow) * a.K + lk;
+  const float* a_src = row_ptr(a.A, a.a_split, tr, tr.v0 + arow, a.K) + lk;
   int brow;
   if constexpr (kGateUp) {
     const int i = nt * 32 + (lrow & 31);
@@ -98,7 +114,8 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_f32(GemmArgs a) {
   for (int r = 0; r < 4; ++r) {
     const int row = ty * 4 + r;
     if (row >= mrows) continue;
-    float* crow = a.C + (int64_t)(m0 + row) * a.ncols;
+    const float* const cbase[2] = {a.C[0], a.C[1]};
+    float* crow = (float*)row_ptr(cbase, a.c_split, tr, tr.v0 + row, a.ncols);
     if constexpr (kGateUp) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -118,14 +135,19 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_f32(GemmArgs a) {
   }
 }
 
-hipError_t launch(bool gate_up, const Shape& s, int64_t rows_bound, const void* A,
-                  const int32_t* off, const void* B, void* C, hipStream_t st) {
-  if (rows_bound <= 0) return hipSuccess;
+hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void* B,
+                  hipStream_t st) {
+  if (io.rows_bound <= 0) return hipSuccess;
   GemmArgs a{};
-  a.A = (const float*)A;
+  a.A[0] = (const float*)io.a[0];
+  a.A[1] = (const float*)(io.a_split ? io.a[1] : io.a[0]);
+  a.C[0] = (float*)io.c[0];
+  a.C[1] = (float*)(io.c_split ? io.c[1] : io.c[0]);
+  a.off0 = io.off[0];
+  a.off1 = io.off[1];
+  a.a_split = io.a_split && io.off[1];
+  a.c_split = io.c_split && io.off[1];
   a.B = (const float*)B;
-  a.C = (float*)C;
-  a.off = off;
   a.E = s.E;
   a.I = s.I;
   if (gate_up) {
@@ -139,7 +161,7 @@ hipError_t launch(bool gate_up, const Shape& s, int64_t rows_bound, const void* 
     a.n_tiles = (s.H + BN - 1) / BN;
     a.b_expert_stride = (int64_t)s.H * s.I;
   }
-  const int64_t grid = m_tiles_bound(rows_bound, s.E, BM) * a.n_tiles;
+  const int64_t grid = xcd_grid(m_tiles_bound(io.rows_bound, s.E, BM), a.n_tiles);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (gate_up)
     hipLaunchKernelGGL(grouped_gemm_f32<true>, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
@@ -150,16 +172,14 @@ hipError_t launch(bool gate_up, const Shape& s, int64_t rows_bound, const void* 
 
 }  // namespace
 
-hipError_t launch_gate_up_f32(const Shape& s, int64_t rows_bound, const void* x_perm,
-                              const int32_t* offsets_c, const void* w_gate_up, void* act,
+hipError_t launch_gate_up_f32(const Shape& s, const GroupedIO& io, const void* w_gate_up,
                               hipStream_t st) {
-  return launch(true, s, rows_bound, x_perm, offsets_c, w_gate_up, act, st);
+  return launch(true, s, io, w_gate_up, st);
 }
 
-hipError_t launch_down_f32(const Shape& s, int64_t rows_bound, const void* act,
-                           const int32_t* offsets_c, const void* w_down, void* y,
+hipError_t launch_down_f32(const Shape& s, const GroupedIO& io, const void* w_down,
                            hipStream_t st) {
-  return launch(false, s, rows_bound, act, offsets_c, w_down, y, st);
+  return launch(false, s, io, w_down, st);
 }
 
 }  // namespace moe

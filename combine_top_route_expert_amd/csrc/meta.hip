@@ -7,7 +7,8 @@
 // AlltoAllV收发异构复用特性": the send lists stay on the device and combine
 // reuses dispatch's lists (here dst_row), so nothing is copied to the host.
 //
-// Three launches, all atomics-free and deterministic:
+// Three launches, deterministic (LDS atomics only add counts, whose sum does
+// not depend on order):
 //  1. meta_hist : one wave per segment of kMetaSeg assignments (segments never
 //     straddle a chunk).  Lanes with equal expert id find each other with one
 //     ballot per id bit; the lowest such lane adds the group's popcount to the
@@ -97,14 +98,17 @@ __global__ void __launch_bounds__(64) meta_hist(MetaArgs a) {
     load_batch(a, b0, f_hi, lane, &b);
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
+      if (b0 + g * 64 >= f_hi) break;
       const int e = b.e[g];
       const bool ok = b.active[g] && e >= 0 && e < a.E;
       invalid += (b.active[g] && !ok) ? 1 : 0;
       const uint64_t peers = peer_mask(e, ok, a.id_bits);
-      if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) cnt[e] += __popcll(peers);
-      __syncthreads();
+      // one add per distinct expert of the group; the total does not depend on order
+      if (ok && (__ffsll((unsigned long long)peers) - 1) == lane)
+        atomicAdd(&cnt[e], (int)__popcll(peers));
     }
   }
+  __syncthreads();
   int32_t* out = a.seg_counts + (size_t)blockIdx.x * a.E;
   for (int e = lane; e < a.E; e += 64) out[e] = cnt[e];
   for (int d = 32; d > 0; d >>= 1) invalid += __shfl_xor(invalid, d);
@@ -208,17 +212,21 @@ __global__ void __launch_bounds__(64) meta_rank(MetaArgs a) {
     load_batch(a, b0, f_hi, lane, &b);
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
+      if (b0 + g * 64 >= f_hi) break;
       const int f = b0 + g * 64 + lane;
       const int e = b.e[g];
       const bool ok = b.active[g] && e >= 0 && e < a.E;
       const uint64_t peers = peer_mask(e, ok, a.id_bits);
-      int row = -1;
-      if (ok) row = base[e] + __popcll(peers & lt);
-      __syncthreads();  // every lane has read base[] before the leaders advance it
-      if (ok && (__ffsll((unsigned long long)peers) - 1) == lane) base[e] += __popcll(peers);
+      const int leader = ok ? __ffsll((unsigned long long)peers) - 1 : lane;
+      // the leader takes the group's rows from its expert's running base (groups
+      // of earlier lanes and earlier iterations come first: program order of
+      // one wave); every peer adds its rank among the group's lanes
+      int first = 0;
+      if (ok && leader == lane) first = atomicAdd(&base[e], (int)__popcll(peers));
+      first = __shfl(first, leader);
+      const int row = ok ? first + __popcll(peers & lt) : -1;
       if (b.active[g]) a.dst_row[f] = row;
       if (ok) a.src_row[cf0 + row] = f;
-      __syncthreads();
     }
   }
 }

@@ -27,7 +27,7 @@ inline void chunk_tokens(const Shape& s, int c, int* t0, int* t1) {
 
 // ---- routing metadata (meta.hip) -------------------------------------------
 constexpr int kMaxExperts = 1024;  // largest E the library accepts
-constexpr int kMetaSeg = 1024;     // segment granule, in assignments (one wave per segment)
+constexpr int kMetaSeg = 256;      // segment granule, in assignments (one wave per segment)
 constexpr int kScanStage = 16384;  // ints of one chunk's [segments][E] block staged in LDS
 
 struct MetaPlan {
@@ -51,18 +51,28 @@ hipError_t launch_combine(const Shape& s, int t0, int t1, const void* y,
                           const int32_t* dst_row, const float* w, void* out, hipStream_t st);
 
 // ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----------------------------
-// `rows_bound` is the chunk's assignment count; `offsets_c` the chunk's E+1 offsets.
-hipError_t launch_gate_up_bf16(const Shape& s, int64_t rows_bound, const void* x_perm,
-                               const int32_t* offsets_c, const void* w_gate_up, void* act,
+// One grouped GEMM over the rows of one chunk, or of the two chunks of a pair.
+// Expert e's rows are the chunk-0 block [off0[e], off0[e+1]) followed by the
+// chunk-1 block [off1[e], off1[e+1]) (none when off1 is null): the expert is
+// multiplied once per launch, so its weights are streamed once for both chunks.
+// A side that is "split" holds the two chunks in two buffers at their own
+// chunk-local rows; a "joint" side is one buffer in which expert e's rows start
+// at off0[e] + off1[e] (the pair's rows grouped by expert; for one chunk this is
+// the chunk's own layout).
+struct GroupedIO {
+  const void* a[2];      // A: [rows][K]; a[1] used when a_split
+  void* c[2];            // C: [rows][ncols]; c[1] used when c_split
+  const int32_t* off[2]; // E + 1 chunk-local offsets of each chunk; off[1] may be null
+  bool a_split, c_split;
+  int64_t rows_bound;    // total rows of the launch (host-known bound)
+};
+hipError_t launch_gate_up_bf16(const Shape& s, const GroupedIO& io, const void* w_gate_up,
                                hipStream_t st);
-hipError_t launch_down_bf16(const Shape& s, int64_t rows_bound, const void* act,
-                            const int32_t* offsets_c, const void* w_down, void* y,
+hipError_t launch_down_bf16(const Shape& s, const GroupedIO& io, const void* w_down,
                             hipStream_t st);
-hipError_t launch_gate_up_f32(const Shape& s, int64_t rows_bound, const void* x_perm,
-                              const int32_t* offsets_c, const void* w_gate_up, void* act,
+hipError_t launch_gate_up_f32(const Shape& s, const GroupedIO& io, const void* w_gate_up,
                               hipStream_t st);
-hipError_t launch_down_f32(const Shape& s, int64_t rows_bound, const void* act,
-                           const int32_t* offsets_c, const void* w_down, void* y,
+hipError_t launch_down_f32(const Shape& s, const GroupedIO& io, const void* w_down,
                            hipStream_t st);
 
 // ---- small device helpers ----------------------------------------------------
@@ -70,48 +80,118 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (1ull << __lane_id()) - 1ull;
 }
 
-// Grouped-GEMM tile lookup.  Expert e owns rows [off[e], off[e+1]) and
-// ceil(rows_e / BM) m-tiles; m-tiles are numbered expert by expert.  Every wave
-// of the calling workgroup runs this independently (one wave scan over E
-// experts, E/64 per lane) and gets the same answer.  Returns false for m-tile
-// indices past the last tile (surplus workgroups of the host-bounded grid).
-__device__ __forceinline__ bool find_m_tile(const int32_t* __restrict__ off, int E, int BM,
-                                            int mt, int* e_out, int* m0_out, int* rows_out) {
-  const int lane = __lane_id();
-  const int per = (E + 63) >> 6;
-  const int e_begin = lane * per;
-  const int e_end = e_begin + per < E ? e_begin + per : E;
-  int sum = 0;
-  for (int e = e_begin; e < e_end; ++e) sum += (off[e + 1] - off[e] + BM - 1) / BM;
-  int incl = sum;
-  for (int d = 1; d < 64; d <<= 1) {
-    int n = __shfl_up(incl, d);
-    if (lane >= d) incl += n;
+// Rows of one m-tile: expert e, virtual rows [v0, v0 + rows) of the expert's
+// concatenated block (chunk-0 rows, then chunk-1 rows).
+struct TileRows {
+  int e, v0, rows;
+  int lo0, n0, lo1;  // chunk-0 first row and count; chunk-1 first row (0 if none)
+
+  // Row index of virtual row v on a split side: (buffer, row).
+  __device__ __forceinline__ int split_row(int v, int* part) const {
+    *part = v >= n0;
+    return v < n0 ? lo0 + v : lo1 + (v - n0);
   }
-  const int total = __shfl(incl, 63);
-  if (mt >= total) return false;
-  const int excl = incl - sum;
-  const uint64_t own = __ballot(excl <= mt && mt < incl);
-  const int owner = __ffsll((unsigned long long)own) - 1;
-  int fe = 0, fm0 = 0, frows = 0;
-  if (lane == owner) {
-    int acc = excl;
-    for (int e = e_begin; e < e_end; ++e) {
-      const int lo = off[e], n = off[e + 1] - lo;
-      const int t = (n + BM - 1) / BM;
-      if (mt < acc + t) {
-        fe = e;
-        fm0 = lo + (mt - acc) * BM;
-        frows = lo + n - fm0 < BM ? lo + n - fm0 : BM;
-        break;
-      }
-      acc += t;
+  // Row index of virtual row v on a joint side.
+  __device__ __forceinline__ int joint_row(int v) const { return lo0 + lo1 + v; }
+};
+
+// Grouped-GEMM tile map.  Expert e owns n_e rows (its rows in one or two
+// chunks) and ceil(n_e / BM) m-tiles; m-tiles are numbered expert by expert.
+// A map can be restricted to a class of experts by row count, so that one
+// launch covers long expert blocks with a large tile and another the short
+// ones.  Every wave of a workgroup builds the map independently (one wave scan
+// over E experts, E/64 per lane) and gets the same answer.
+struct MTileMap {
+  int total;              // m-tiles of all experts in the class
+  int excl, incl;         // this lane's m-tile range
+  int e_begin, e_end;     // this lane's experts
+  int lo_rows, hi_rows;   // class: experts with lo_rows <= rows < hi_rows
+
+  __device__ __forceinline__ int tiles_of(int n, int BM) const {
+    return (n >= lo_rows && n < hi_rows) ? (n + BM - 1) / BM : 0;
+  }
+
+  static __device__ __forceinline__ int rows_of(const int32_t* __restrict__ off0,
+                                                const int32_t* __restrict__ off1, int e) {
+    int n = off0[e + 1] - off0[e];
+    if (off1) n += off1[e + 1] - off1[e];
+    return n;
+  }
+
+  __device__ __forceinline__ void build(const int32_t* __restrict__ off0,
+                                        const int32_t* __restrict__ off1, int E, int BM,
+                                        int lo = 1, int hi = 0x7fffffff) {
+    lo_rows = lo;
+    hi_rows = hi;
+    const int lane = __lane_id();
+    const int per = (E + 63) >> 6;
+    e_begin = lane * per;
+    e_end = e_begin + per < E ? e_begin + per : E;
+    int sum = 0;
+    for (int e = e_begin; e < e_end; ++e) sum += tiles_of(rows_of(off0, off1, e), BM);
+    incl = sum;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int n = __shfl_up(incl, d);
+      if (lane >= d) incl += n;
     }
+    excl = incl - sum;
+    total = __shfl(incl, 63);
   }
-  *e_out = __shfl(fe, owner);
-  *m0_out = __shfl(fm0, owner);
-  *rows_out = __shfl(frows, owner);
-  return true;
+
+  // Rows of m-tile mt (< total), for all lanes.
+  __device__ __forceinline__ TileRows locate(const int32_t* __restrict__ off0,
+                                             const int32_t* __restrict__ off1, int BM,
+                                             int mt) const {
+    const int lane = __lane_id();
+    const uint64_t own = __ballot(excl <= mt && mt < incl);
+    const int owner = __ffsll((unsigned long long)own) - 1;
+    int fe = 0, fv0 = 0, frows = 0, flo0 = 0, fn0 = 0, flo1 = 0;
+    if (lane == owner) {
+      int acc = excl;
+      for (int e = e_begin; e < e_end; ++e) {
+        const int n = rows_of(off0, off1, e);
+        const int t = tiles_of(n, BM);
+        if (mt < acc + t) {
+          fe = e;
+          fv0 = (mt - acc) * BM;
+          frows = n - fv0 < BM ? n - fv0 : BM;
+          flo0 = off0[e];
+          fn0 = off0[e + 1] - flo0;
+          flo1 = off1 ? off1[e] : 0;
+          break;
+        }
+        acc += t;
+      }
+    }
+    TileRows r;
+    r.e = __shfl(fe, owner);
+    r.v0 = __shfl(fv0, owner);
+    r.rows = __shfl(frows, owner);
+    r.lo0 = __shfl(flo0, owner);
+    r.n0 = __shfl(fn0, owner);
+    r.lo1 = __shfl(flo1, owner);
+    return r;
+  }
+};
+
+// Workgroup -> (m-tile, n-tile).  Workgroup b runs on XCD b % 8; each XCD gets
+// a contiguous range of ceil(total/8) m-tiles with all their n-tiles, in order,
+// so an m-tile's activation panel and an expert's weight panels are fetched
+// into one XCD's L2 instead of up to eight.  The grid has 8 * ceil(bound/8) *
+// n_tiles workgroups; those past their XCD's range exit.
+__device__ __forceinline__ bool xcd_tile(int total, int n_tiles, int* mt, int* nt) {
+  const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int ml = q / n_tiles;
+  if (ml >= per) return false;
+  *mt = x * per + ml;
+  *nt = q - ml * n_tiles;
+  return *mt < total;
+}
+
+// Host side: grid of xcd_tile for a bound on the m-tiles.
+inline int64_t xcd_grid(int64_t m_tiles_bound, int n_tiles) {
+  return 8 * ((m_tiles_bound + 7) / 8) * (int64_t)n_tiles;
 }
 
 // Upper bound on the m-tiles of a grouped GEMM over `rows` rows split among E

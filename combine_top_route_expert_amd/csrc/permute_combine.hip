@@ -32,7 +32,8 @@ permute_rows(const u32x4* __restrict__ hidden, const int32_t* __restrict__ dst_r
   const int t = t0 + blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= t1) return;
   const u32x4* src = hidden + (size_t)t * nvec;
-  const int32_t* dr = dst_row + (size_t)t * k;
+  // the token's k destination rows, one per lane, fetched in one round trip
+  const int my_row = lane < k ? dst_row[(size_t)t * k + lane] : -1;
   for (int v0 = 0; v0 < nvec; v0 += 64 * kVecPerLane) {
     u32x4 buf[kVecPerLane];
 #pragma unroll
@@ -41,7 +42,7 @@ permute_rows(const u32x4* __restrict__ hidden, const int32_t* __restrict__ dst_r
       if (v < nvec) buf[i] = src[v];
     }
     for (int j = 0; j < k; ++j) {
-      const int r = dr[j];
+      const int r = __shfl(my_row, j);
       if (r < 0) continue;
       u32x4* dst = x_perm + (size_t)r * nvec;
 #pragma unroll
@@ -82,33 +83,50 @@ combine_rows(const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
   const int lane = threadIdx.x & 63;
   const int t = t0 + blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= t1) return;
-  const int32_t* dr = dst_row + (size_t)t * k;
-  const float* wt = w + (size_t)t * k;
+  // the token's k rows and weights, one slot per lane, fetched in one round trip
+  const int my_row = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
   for (int v0 = 0; v0 < nvec; v0 += 64 * kVecPerLane) {
     float acc[kVecPerLane][kEl];
 #pragma unroll
     for (int i = 0; i < kVecPerLane; ++i)
 #pragma unroll
       for (int q = 0; q < kEl; ++q) acc[i][q] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = dr[j];
-      if (r < 0) continue;
-      const float wj = wt[j];
-      const u32x4* src = y + (size_t)r * nvec;
+    // slots in groups of four: the group's row loads are all issued before
+    // any is accumulated; accumulation stays in ascending slot order
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      u32x4 rows[4][kVecPerLane];
+      int rj[4];
+      float wj[4];
 #pragma unroll
-      for (int i = 0; i < kVecPerLane; ++i) {
-        int v = v0 + i * 64 + lane;
-        if (v < nvec) {
-          u32x4 q = src[v];
-          float f[kEl];
-          if constexpr (kBf16) {
-            unpack_bf16x8(q, f);
-          } else {
+      for (int g = 0; g < 4; ++g) {
+        rj[g] = j0 + g < k ? __shfl(my_row, j0 + g) : -1;
+        wj[g] = __shfl(my_w, (j0 + g) & 63);
+        if (rj[g] < 0) continue;
+        const u32x4* src = y + (size_t)rj[g] * nvec;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(q[e]);
+        for (int i = 0; i < kVecPerLane; ++i) {
+          const int v = v0 + i * 64 + lane;
+          if (v < nvec) rows[g][i] = src[v];
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (rj[g] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < kVecPerLane; ++i) {
+          const int v = v0 + i * 64 + lane;
+          if (v < nvec) {
+            float f[kEl];
+            if constexpr (kBf16) {
+              unpack_bf16x8(rows[g][i], f);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(rows[g][i][q]);
+            }
+#pragma unroll
+            for (int q = 0; q < kEl; ++q) acc[i][q] = __builtin_fmaf(wj[g], f[q], acc[i][q]);
           }
-#pragma unroll
-          for (int e = 0; e < kEl; ++e) acc[i][e] = __builtin_fmaf(wj, f[e], acc[i][e]);
         }
       }
     }

@@ -21,8 +21,8 @@
  * ---------------------------------------
  *  - Pointers named as tensors are DEVICE memory owned by the caller.  The
  *    library allocates no device memory and keeps no pointer after it returns.
- *    Its only state is a per-thread cache of two HIP events per device, used by
- *    moe_chunked_forward to order its two streams.
+ *    Its only state is a per-thread cache of three HIP events per device, used
+ *    by moe_chunked_forward(_schedule) to order its two streams.
  *  - Calls only enqueue work on the given stream(s) and return.  No call waits
  *    on the device or copies anything back to the host.
  *  - Row-major, dense layouts:
@@ -69,6 +69,12 @@ typedef enum moe_status {
 } moe_status;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Stream schedule of moe_chunked_forward_schedule (see there). */
+typedef enum moe_schedule {
+  MOE_SCHEDULE_PAIR_FUSED = 0,  /* one expert-GEMM launch pair per chunk pair (default) */
+  MOE_SCHEDULE_PER_CHUNK = 1    /* every chunk runs all four steps on its own stream */
+} moe_schedule;
 
 /* Problem shape.  Field names follow the pages' notation. */
 typedef struct moe_shape {
@@ -171,6 +177,40 @@ moe_status moe_expert_ffn(const moe_shape* shape, int32_t chunk, const void* x_p
                           void* act, void* y, hipStream_t stream);
 
 /*
+ * Expert GEMMs of the two chunks of a pair, chunk and chunk + 1, each as ONE
+ * grouped launch over both chunks' rows (the pair residency W_pair of the
+ * MindSpeed Chunk MoE key formulas: both chunks' rows are resident together, so
+ * each expert's weights are streamed once for the pair instead of once per
+ * chunk).  Row for row the same arithmetic as the single-chunk calls, so the
+ * same bits.
+ *
+ *  x_perm0, y0  chunk `chunk`'s buffers of rows0 = (t1-t0)*k rows of H
+ *               (y0 may alias x_perm0)
+ *  x_perm1, y1  chunk `chunk+1`'s buffers of rows1 rows of H (y1 may alias
+ *               x_perm1); ignored, and may be null, when chunk + 1 == N or that
+ *               chunk is empty (then the call is the single-chunk one)
+ *  act          [rows0 + rows1][I]: the pair's rows grouped by expert; expert
+ *               e's rows start at offsets[chunk][e] + offsets[chunk+1][e], its
+ *               chunk-`chunk` rows first (for a lone chunk: that chunk's layout)
+ *  offsets      the full [N][E+1] array
+ * A pair with no rows is a no-op that needs no pointer.  Rows past each chunk's
+ * valid rows are not written.
+ */
+moe_status moe_expert_gate_up_pair(const moe_shape* shape, int32_t chunk, const void* x_perm0,
+                                   const void* x_perm1, const int32_t* offsets,
+                                   const void* w_gate_up, void* act, hipStream_t stream);
+
+moe_status moe_expert_down_pair(const moe_shape* shape, int32_t chunk, const void* act,
+                                const int32_t* offsets, const void* w_down, void* y0, void* y1,
+                                hipStream_t stream);
+
+/* moe_expert_gate_up_pair followed by moe_expert_down_pair on the same stream. */
+moe_status moe_expert_ffn_pair(const moe_shape* shape, int32_t chunk, const void* x_perm0,
+                               const void* x_perm1, const int32_t* offsets,
+                               const void* w_gate_up, const void* w_down, void* act, void* y0,
+                               void* y1, hipStream_t stream);
+
+/*
  * Unpermute and weighted combine of chunk `chunk` (MindSpeed Chunk MoE article,
  * timing-diagram section; the combine reuses dispatch's dst_row, as the
  * MindSpore page's "# 02" reuses the dispatch lists):
@@ -187,13 +227,27 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  * diagram and key formulas; Ascend dual-stream article, "01 Prefill
  * micro-batch" overlap of one micro-batch's compute with another's transfer).
  *
- * Metadata for all chunks runs once on s0.  Chunk c then runs permute ->
- * gate_up -> down -> combine on stream s[c % 2] in workspace slot c % 2, so the
- * two chunks of a pair are in flight together and at most two chunks are
- * resident.  s1 == s0 is legal and gives the same bits without overlap; the
- * result never depends on N.  On return s0 is ordered after all work of the
- * call.  ws must hold moe_workspace_size bytes.  dev_error is nullable.
+ * Metadata for all chunks runs once on s0.  Adjacent chunks (0,1), (2,3), ...
+ * form pairs; at most two chunks are resident (workspace slots 0 and 1), and a
+ * last odd chunk runs alone.
+ *  MOE_SCHEDULE_PAIR_FUSED: permute c on s0 while permute c+1 runs on s1; one
+ *    gate_up and one down launch over the pair's rows on s0 (moe_expert_ffn_pair);
+ *    combine c on s0 while combine c+1 runs on s1.
+ *  MOE_SCHEDULE_PER_CHUNK: chunk c runs permute -> gate_up -> down -> combine on
+ *    stream s[c % 2] in slot c % 2, so the two chunks of a pair overlap as whole
+ *    pipelines; every chunk streams the expert weights again.
+ * s1 == s0 (or null) is legal and gives the same bits without overlap; the
+ * result never depends on N or on the schedule.  On return s0 is ordered after
+ * all work of the call.  ws must hold moe_workspace_size bytes.  dev_error is
+ * nullable.  schedule outside moe_schedule -> MOE_ERR_INVALID_ARG.
  */
+moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidden_states,
+                                        const int32_t* top_k_index, const float* top_k_weights,
+                                        const void* w_gate_up, const void* w_down, void* out,
+                                        int32_t* dev_error, void* ws, size_t ws_bytes,
+                                        hipStream_t s0, hipStream_t s1, int32_t schedule);
+
+/* moe_chunked_forward_schedule with MOE_SCHEDULE_PAIR_FUSED. */
 moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states,
                                const int32_t* top_k_index, const float* top_k_weights,
                                const void* w_gate_up, const void* w_down, void* out,

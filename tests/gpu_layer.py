@@ -93,7 +93,7 @@ def run_route_meta(idx: torch.Tensor, shape: moe.moe_shape):
 
 
 def run_forward(layer: Layer, shape: moe.moe_shape, two_streams: bool = True,
-                out: Optional[torch.Tensor] = None):
+                out: Optional[torch.Tensor] = None, schedule: Optional[int] = None):
     c = layer.cfg
     if out is None:
         out = torch.full((c.T, c.H), float("nan"), dtype=c.torch_dtype, device="cuda")
@@ -101,8 +101,12 @@ def run_forward(layer: Layer, shape: moe.moe_shape, two_streams: bool = True,
     err = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream() if two_streams else None
-    moe.moe_chunked_forward(shape, layer.hidden, layer.idx, layer.w, layer.wgu, layer.wd, out, ws,
-                            err, s0=s0, s1=s1)
+    if schedule is None:
+        moe.moe_chunked_forward(shape, layer.hidden, layer.idx, layer.w, layer.wgu, layer.wd, out,
+                                ws, err, s0=s0, s1=s1)
+    else:
+        moe.moe_chunked_forward_schedule(shape, layer.hidden, layer.idx, layer.w, layer.wgu,
+                                         layer.wd, out, ws, err, s0=s0, s1=s1, schedule=schedule)
     torch.cuda.synchronize()
     return out, int(err.item())
 

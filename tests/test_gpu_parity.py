@@ -236,10 +236,66 @@ def test_chunked_equals_unchunked_bitwise(name, Ns):
     L = layer_for(name)
     base, _ = run_forward(L, L.shape(1), two_streams=False)
     for N in Ns:
-        for two in (True, False):
-            say(f"chunked {name} N={N} two_streams={two}")
-            out, _ = run_forward(L, L.shape(N), two_streams=two)
-            assert torch.equal(out, base), (N, two)
+        for sched in (moe.MOE_SCHEDULE_PAIR_FUSED, moe.MOE_SCHEDULE_PER_CHUNK):
+            for two in (True, False):
+                say(f"chunked {name} N={N} schedule={sched} two_streams={two}")
+                out, _ = run_forward(L, L.shape(N), two_streams=two, schedule=sched)
+                assert torch.equal(out, base), (N, sched, two)
+
+
+PAIR_CASES = [("bf16_e64_zipf", 2, 0), ("tiny_f32", 3, 0), ("tiny_f32", 3, 2), ("t3_n4", 4, 2),
+              ("packed16k_e128", 4, 2), ("dsv3_e256", 3, 0), ("dsv3_e256", 3, 2),
+              ("decode_t64", 2, 0)]
+
+
+@pytest.mark.parametrize("name,N,c", PAIR_CASES)
+def test_expert_ffn_pair_bitwise(name, N, c):
+    """One launch pair over chunks c and c+1 == moe_expert_ffn on each chunk, bit
+    for bit; act holds the pair's rows grouped by expert; rows past each chunk's
+    valid rows are not written."""
+    L = layer_for(name)
+    cfg = L.cfg
+    shape = L.shape(N)
+    meta = run_route_meta(L.idx, shape)
+    dst = torch.from_numpy(meta["dst_row"]).cuda()
+    off = torch.from_numpy(meta["offsets"]).cuda()
+    dt = cfg.torch_dtype
+    chunks = [c] + ([c + 1] if c + 1 < N else [])
+    rows = {}
+    xp, ref_act, ref_y = {}, {}, {}
+    for cc in chunks:
+        t0, t1 = moe.moe_chunk_range(shape, cc)
+        rows[cc] = (t1 - t0) * cfg.k
+        xp[cc] = torch.empty((rows[cc], cfg.H), dtype=dt, device="cuda")
+        if rows[cc]:
+            moe.moe_permute(shape, cc, L.hidden, dst, xp[cc])
+            ref_act[cc] = torch.empty((rows[cc], cfg.I), dtype=dt, device="cuda")
+            ref_y[cc] = torch.empty((rows[cc], cfg.H), dtype=dt, device="cuda")
+            say(f"ffn {name} N={N} chunk={cc}")
+            moe.moe_expert_ffn(shape, cc, xp[cc], off, L.wgu, L.wd, ref_act[cc], ref_y[cc])
+    r1 = rows.get(c + 1, 0)
+    act = torch.full((rows[c] + r1, cfg.I), 555.0, dtype=dt, device="cuda")
+    y0 = torch.full((rows[c] + 3, cfg.H), 777.0, dtype=dt, device="cuda")
+    y1 = torch.full((r1 + 3, cfg.H), 777.0, dtype=dt, device="cuda") if r1 else None
+    say(f"ffn_pair {name} N={N} chunk={c}")
+    moe.moe_expert_ffn_pair(shape, c, xp[c], xp.get(c + 1) if r1 else None, off, L.wgu, L.wd,
+                            act, y0, y1)
+    torch.cuda.synchronize()
+    o0 = meta["offsets"][c]
+    o1 = meta["offsets"][c + 1] if r1 else np.zeros_like(o0)
+    valid0, valid1 = int(o0[-1]), int(o1[-1])
+    assert torch.equal(y0[:valid0], ref_y[c][:valid0])
+    assert bool((y0[valid0:] == 777.0).all())
+    if r1:
+        assert torch.equal(y1[:valid1], ref_y[c + 1][:valid1])
+        assert bool((y1[valid1:] == 777.0).all())
+    for e in range(cfg.E):
+        n0, n1 = int(o0[e + 1] - o0[e]), int(o1[e + 1] - o1[e])
+        b = int(o0[e] + o1[e])
+        assert torch.equal(act[b:b + n0], ref_act[c][int(o0[e]):int(o0[e]) + n0]), e
+        if n1:
+            assert torch.equal(act[b + n0:b + n0 + n1], ref_act[c + 1][int(o1[e]):int(o1[e]) + n1]), e
+    assert bool((act[valid0 + valid1:] == 555.0).all())
 
 
 def test_run_twice_identical():
@@ -269,6 +325,19 @@ def test_steps_compose_to_forward():
         moe.moe_unpermute_combine(shape, c, xp, dst, L.w, out)
     torch.cuda.synchronize()
     assert torch.equal(out, fwd)
+    # the same with the pair-fused FFN
+    xps = []
+    for c in range(2):
+        t0, t1 = moe.moe_chunk_range(shape, c)
+        xps.append(torch.empty(((t1 - t0) * cfg.k, cfg.H), dtype=cfg.torch_dtype, device="cuda"))
+        moe.moe_permute(shape, c, L.hidden, dst, xps[c])
+    act = torch.empty((cfg.T * cfg.k, cfg.I), dtype=cfg.torch_dtype, device="cuda")
+    moe.moe_expert_ffn_pair(shape, 0, xps[0], xps[1], off, L.wgu, L.wd, act, xps[0], xps[1])
+    out2 = torch.zeros_like(fwd)
+    for c in range(2):
+        moe.moe_unpermute_combine(shape, c, xps[c], dst, L.w, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, fwd)
 
 
 def test_dropped_ids_and_canary_rows():
@@ -281,9 +350,9 @@ def test_dropped_ids_and_canary_rows():
     idx[9, 1] = cfg.E
     idx[200, 0] = 1 << 20
     L = build_layer(cfg, idx, w)
-    for N in (1, 3):
+    for N, sched in ((1, None), (3, moe.MOE_SCHEDULE_PAIR_FUSED), (3, moe.MOE_SCHEDULE_PER_CHUNK)):
         out = torch.full((cfg.T + 2, cfg.H), 777.0, dtype=cfg.torch_dtype, device="cuda")
-        got, err = run_forward(L, L.shape(N), out=out)
+        got, err = run_forward(L, L.shape(N), out=out, schedule=sched)
         ref, meta = oracle.moe_forward(L.hidden64(), idx, w, L.expert64, cfg.E, cfg.I, 1, N)
         assert err == meta["n_invalid"] == cfg.k + 2
         assert oracle.row_rel_err(f64(got[:cfg.T]), ref) <= TOL["f32"]

@@ -140,6 +140,17 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert _raw("moe_expert_down", sp, 0, None, fake, fake, fake, None) == 1
     assert _raw("moe_unpermute_combine", sp, 0, fake, fake, fake, fake + 4, None) == 1
     assert _raw("moe_expert_ffn", sp, 0, fake, None, fake, fake, fake, fake, None) == 1
+    # pair FFN: null second-chunk buffers while chunk 1 has rows, misaligned act, bad chunk
+    assert _raw("moe_expert_ffn_pair", sp, 0, fake, None, fake, fake, fake, fake, fake, fake,
+                None) == 1
+    assert _raw("moe_expert_ffn_pair", sp, 0, fake, fake, fake, fake, fake, fake + 2, fake,
+                fake, None) == 1
+    assert _raw("moe_expert_ffn_pair", sp, 2, fake, fake, fake, fake, fake, fake, fake, fake,
+                None) == 1
+    # unknown schedule
+    for sched in (-1, 2):
+        assert _raw("moe_chunked_forward_schedule", sp, fake, fake, fake, fake, fake, fake, None,
+                    fake, need, None, None, sched) == 1
 
 
 def test_empty_chunk_calls_are_noops():
@@ -150,6 +161,9 @@ def test_empty_chunk_calls_are_noops():
     assert _raw("moe_permute", sp, 3, None, None, None, None) == 0
     assert _raw("moe_expert_ffn", sp, 3, None, None, None, None, None, None, None) == 0
     assert _raw("moe_unpermute_combine", sp, 3, None, None, None, None, None) == 0
+    # a pair whose chunks are both empty; none of its pointers is needed
+    assert _raw("moe_expert_ffn_pair", sp, 3, None, None, None, None, None, None, None, None,
+                None) == 0
 
 
 def test_binding_refuses_host_tensors():
