@@ -212,8 +212,8 @@ def cpu_baseline(cfg, inp, synth, target_s=15.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="bf16_e64_zipf")
     ap.add_argument("--num-chunks", type=int, default=2)
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -238,6 +238,9 @@ def main():
     inp = make_inputs(cfg, torch, synth)
     shape = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, N, cfg.dtype)
 
+    # one common warm-up (clocks, caches, allocator) before any timed run
+    log("warm-up")
+    time_layer(moe, torch, shape, inp, 1, max(args.warmup, 20))
     log(f"layer N={N}")
     main_run = time_layer(moe, torch, shape, inp, args.steps, args.warmup)
     log(f"layer N=1 (reference)")

@@ -2,21 +2,22 @@
 //
 // The expert computation of the MindSpeed Chunk MoE article (core principle /
 // timing-diagram sections) is read as a SwiGLU FFN per expert; each expert
-// multiplies its contiguous block of permuted rows:
+// multiplies its block of permuted rows:
 //   gate_up: act[r][i] = silu(x_r . Wg[e][i]) * (x_r . Wu[e][i])   (K = H)
 //   down   : y[r][n]   = act_r . Wd[e][n]                          (K = I)
 // Both operands are K-contiguous ([rows][K] activations, [cols][K] weights).
+// One launch covers one chunk or both chunks of a pair (GroupedIO): an
+// expert's rows are its rows in the first chunk followed by its rows in the
+// second, so its weights are streamed once per launch.
 //
-// Pipeline: K advances 64 at a time.  Each stage of the A (rows) and B
+// Pipeline: K advances BK (64) at a time.  Each stage of the A (rows) and B
 // (weight) tiles is copied global -> LDS by the direct-to-LDS load
 // (global_load_lds_dwordx4: 64 lanes x 16 bytes land as one contiguous 1 KB
 // block), so loads need no VGPRs and STAGES-1 stages are in flight while the
 // matrix cores work on the oldest one.  Completion is tracked with explicit
 // vmcnt waits plus a plain s_barrier (no fence that would drain every load).
-// Inside a 1 KB block lane l holds row l/8 and 16-byte slot l%8; the global
-// chunk it fetches is slot ^ ((row >> 1) & 7), which makes the 16-byte fragment
-// reads of 16 consecutive rows hit distinct LDS banks (measured: no bank
-// conflicts).
+// LDS rows are XOR-swizzled (StageGeom) so that 16-byte fragment reads are free
+// of bank conflicts (measured).
 //
 // Matrix instruction: on gfx950 v_mfma_f32_32x32x16_bf16 and
 // v_mfma_f32_16x16x32_bf16 both occupy the matrix pipe for about 32 cycles, so
@@ -34,17 +35,19 @@
 // Grouping: m-tiles of all experts are numbered expert by expert; every
 // workgroup builds that numbering from the device-resident offsets (MTileMap),
 // so the host never reads group sizes.  Each XCD takes a contiguous range of
-// m-tiles with all their n-tiles (xcd_tile), keeping activation and weight
-// panels in one L2.  The grid is bounded from the chunk's assignment count and
-// surplus workgroups exit.  Rows past an expert's block
-// are loaded from a clamped row and never stored.  Two workgroups per CU (or
-// eight waves in one) let one wave's barrier and LDS-read bubbles hide behind
-// another's MFMAs; a persistent variant with deeper prefetch measured slower.
+// m-tiles with all their n-tiles (xcd_tile).  The grid is bounded from the
+// launch's assignment count and surplus workgroups exit.  Rows past an
+// expert's block are loaded from a clamped row (A blocks wholly past it are
+// not loaded at all) and never stored.
 //
-// Instances: a 256 x 256 tile with 8 waves for large GEMMs with long expert
-// blocks or long K / N, a 64 x 128 tile (three workgroups per CU) otherwise.
-// All use the same MFMA instruction and the same order of K steps, so a row
-// gets the same bits from any instance or chunking.
+// What bounds it (measured with per-workgroup timestamps): the MFMA loop alone
+// (no global loads) runs at ~94% of the matrix peak at the clock it gets, and
+// adding the LDS fragment reads costs nothing.  With the operand streaming on
+// top, the chip's power management lowers the shader clock (about 2.2 GHz ->
+// 1.5-2.1 GHz) and a full 256 x 256 tile takes ~1.45x the cycles of its MFMAs.
+// Deeper pipelines (BK 32 with 4-5 stages, a third weight buffer),
+// register-staged loads, loads interleaved with the MFMAs, round-robin XCD
+// dealing and 4-wave 128 x 128 wave tiles all measured no faster.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -297,20 +300,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
 }
 
-// Tile instances.  All use the same MFMA instruction and the same order of
-// K steps, so any instance gives the same bits for a row; the choice only
-// affects speed.  A compile-time override forces one instance, for
-// comparisons.
-enum Instance {
-  kAuto = 0,
-  kWide64x2 = 1,    // 256 x 256, 8 waves, BK 64, 2 stages (128 KB LDS)
-  kWide32x4 = 2,    // 256 x 256, 8 waves, BK 32, 4 stages (128 KB LDS)
-  kWide32x5 = 3,    // 256 x 256, 8 waves, BK 32, 5 stages (160 KB LDS)
-  kTall64x3 = 4,    // 256 x 128, 8 waves, BK 64, 3 stages (144 KB LDS)
-  kNarrow64x2 = 5,  // 64 x 128, 4 waves, BK 64, 2 stages (48 KB LDS, 3 per CU)
-  kNarrow32x4 = 6,  // 64 x 128, 4 waves, BK 32, 4 stages (48 KB LDS, 3 per CU)
-  kMid32x4 = 7,     // 128 x 128, 4 waves, BK 32, 4 stages (64 KB LDS, 2 per CU)
-};
+// Tile instances.  Both use the same MFMA instruction and the same order of
+// K steps, so either gives the same bits for a row; the choice only affects
+// speed.  The wide 256 x 256 tile (8 waves, one workgroup per CU) moves the
+// fewest bytes per MFMA and wins on large GEMMs with long expert blocks or a
+// long K or N; the 64 x 128 tile (three workgroups per CU) wins on small or
+// skewed GEMMs where padding and occupancy matter more.  A compile-time
+// override forces one instance.
+enum Instance { kAuto = 0, kWide = 1, kNarrow = 2 };
 #ifndef MOE_GEMM_FORCE
 #define MOE_GEMM_FORCE 0
 #endif
@@ -341,26 +338,11 @@ hipError_t launch_kind(int inst, GemmArgs a, const Shape& s, int64_t rows_bound,
   const bool wide_ok = !kGateUp || s.I % 128 == 0;
   if (inst == kAuto) {
     const int ncols = kGateUp ? 2 * s.I : s.H;
-    inst = wide_ok && prefer_wide(rows_bound, s.E, a.K, ncols) ? kWide64x2 : kNarrow64x2;
+    inst = prefer_wide(rows_bound, s.E, a.K, ncols) ? kWide : kNarrow;
   }
-  if (!wide_ok && inst != kNarrow64x2 && inst != kNarrow32x4 && inst != kMid32x4)
-    inst = kNarrow64x2;
-  switch (inst) {
-    case kWide64x2:
-      return launch_instance<kGateUp, 256, 256, 2, 4, 64, 2>(a, s, rows_bound, st);
-    case kWide32x4:
-      return launch_instance<kGateUp, 256, 256, 2, 4, 32, 4>(a, s, rows_bound, st);
-    case kWide32x5:
-      return launch_instance<kGateUp, 256, 256, 2, 4, 32, 5>(a, s, rows_bound, st);
-    case kTall64x3:
-      return launch_instance<kGateUp, 256, 128, 4, 2, 64, 3>(a, s, rows_bound, st);
-    case kNarrow32x4:
-      return launch_instance<kGateUp, 64, 128, 2, 2, 32, 4>(a, s, rows_bound, st);
-    case kMid32x4:
-      return launch_instance<kGateUp, 128, 128, 2, 2, 32, 4>(a, s, rows_bound, st);
-    default:
-      return launch_instance<kGateUp, 64, 128, 2, 2, 64, 2>(a, s, rows_bound, st);
-  }
+  if (inst == kWide && wide_ok)
+    return launch_instance<kGateUp, 256, 256, 2, 4, 64, 2>(a, s, rows_bound, st);
+  return launch_instance<kGateUp, 64, 128, 2, 2, 64, 2>(a, s, rows_bound, st);
 }
 
 hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void* B,

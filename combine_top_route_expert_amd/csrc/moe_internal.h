@@ -174,11 +174,13 @@ struct MTileMap {
   }
 };
 
-// Workgroup -> (m-tile, n-tile).  Workgroup b runs on XCD b % 8; each XCD gets
-// a contiguous range of ceil(total/8) m-tiles with all their n-tiles, in order,
-// so an m-tile's activation panel and an expert's weight panels are fetched
-// into one XCD's L2 instead of up to eight.  The grid has 8 * ceil(bound/8) *
-// n_tiles workgroups; those past their XCD's range exit.
+// Workgroup -> (m-tile, n-tile).  Workgroup b runs on XCD b % 8 (checked
+// against the hardware XCC id); each XCD gets a contiguous range of
+// ceil(total/8) m-tiles with all their n-tiles, in order, so an m-tile's
+// activation panel and an expert's weight panels are fetched into one XCD's L2
+// instead of up to eight (dealing m-tiles round-robin balances the XCDs better
+// but measured no faster: each tile then misses more).  The grid has
+// 8 * ceil(bound/8) * n_tiles workgroups; those past their XCD's range exit.
 __device__ __forceinline__ bool xcd_tile(int total, int n_tiles, int* mt, int* nt) {
   const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int per = (total + 7) >> 3;
