@@ -87,6 +87,34 @@ def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True,
             "workspace_bytes": ws.numel(), "dev_error": int(err.item())}
 
 
+def per_step_times(moe, torch, shape, inp, reps, flush_bytes=0):
+    """Median and minimum of single-step times (HIP events around each step).  With
+    flush_bytes > 0 a scratch buffer of that size is written before every step,
+    outside the timed window, so L2 and MALL start cold."""
+    out = torch.empty((shape.T, shape.H), dtype=shape.torch_dtype, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    times = []
+    for i in range(reps + 2):
+        if scratch is not None:
+            scratch.fill_(i & 0xff)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s0)
+        moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"], inp["wd"],
+                                out, ws, None, s0=s0, s1=s1)
+        e1.record(s0)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1))
+    times.sort()
+    return {"median_ms": times[len(times) // 2], "min_ms": times[0], "reps": reps,
+            "flush_bytes": flush_bytes}
+
+
 def kernel_times(moe, torch, shape, inp, reps):
     """Average duration of each launch the layer makes for its first chunk pair
     (route_meta for all chunks; permute and combine of chunk 0; the gate_up and
@@ -249,6 +277,9 @@ def main():
     log(f"layer N={N}, per-chunk schedule")
     run_pc = time_layer(moe, torch, shape, inp, args.steps, args.warmup,
                         schedule=moe.MOE_SCHEDULE_PER_CHUNK)
+    log("single steps, warm and with L2/MALL flushed")
+    warm = per_step_times(moe, torch, shape, inp, 20)
+    cold = per_step_times(moe, torch, shape, inp, 20, flush_bytes=1 << 30)
     log("per-kernel timing")
     kt, rows0, e_act0, _ = kernel_times(moe, torch, shape, inp, args.kernel_reps)
     copy_bw = copy_bandwidth(torch)
@@ -289,7 +320,9 @@ def main():
         "unchunked": {"ms_per_step": run1["wall_ms"], "value": cfg.T / (run1["wall_ms"] * 1e-3)},
         "per_chunk_schedule": {"ms_per_step": run_pc["wall_ms"],
                                "value": cfg.T / (run_pc["wall_ms"] * 1e-3)},
-        "workspace_bytes": {"N": main_run["workspace_bytes"], "N1": run1["workspace_bytes"]},
+        "single_step": {"warm": warm, "cold": cold},
+        "workspace_bytes": {"N": main_run["workspace_bytes"], "N1": run1["workspace_bytes"],
+                            "slots_model_N": min(N, 2) * -(-cfg.T // N) * cfg.k * (H + I) * s},
         "copy_bandwidth_GBps": copy_bw / 1e9,
         "expert_load": {"max_over_mean": float(inp["counts"].max() / inp["counts"].mean()),
                         "empty_experts": int((inp["counts"] == 0).sum())},

@@ -36,6 +36,13 @@ Readings where the pages are silent (each is listed in the design doc):
 * send splits to G destination groups of E/G contiguous experts are sums of the
   per-expert counts.
 
+Backward (the gradient of the same layer, with the forward of every chunk
+recomputed in the backward pass as the guide's chunk_moe_recompute option does,
+[ChunkMoE, "操作指南" step 3 and the timing-diagram section, whose backward
+mirrors the forward chunk by chunk]): ``silu_grad``, ``moe_backward``,
+``moe_tokens_backward``, ``expert_weight_grads``.  Pinned by central finite
+differences of the forward oracle.
+
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -47,6 +54,7 @@ import numpy as np
 __all__ = [
     "chunk_bounds", "resolve_num_chunks", "w_pair_rows", "route_meta", "permute",
     "silu", "expert_act", "expert_ffn", "unpermute_combine", "moe_forward", "moe_tokens",
+    "silu_grad", "moe_backward", "moe_tokens_backward", "expert_weight_grads",
 ]
 
 
@@ -256,6 +264,128 @@ def moe_tokens(tokens: Sequence[int], hidden: np.ndarray, top_k_index: np.ndarra
     for j in range(top_k_index.shape[1]):  # ascending slot order
         out += partial[:, j]
     return out
+
+
+# --------------------------------------------------------------------------
+# backward of the whole layer, chunk by chunk with the forward recomputed
+# --------------------------------------------------------------------------
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu / dz = s + z s (1 - s) with s = 1 / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-z))
+    return s + z * s * (1.0 - s)
+
+
+def moe_backward(hidden: np.ndarray, top_k_index: np.ndarray, top_k_weights: np.ndarray,
+                 get_expert: ExpertGetter, E: int, I: int, grad_out: np.ndarray, G: int = 1,
+                 N: int = 1) -> Dict[str, object]:
+    """Gradient of L = sum(grad_out * out) with respect to hidden_states,
+    top_k_weights and every expert's weights, for the chunked layer of
+    ``moe_forward``.  Per chunk: permute again, recompute each expert's g, u, act
+    and y, then
+
+    * combine backward: grad_w[t,j] = grad_out[t] . y[r] and
+      grad_y[r] = w[t,j] grad_out[t] for r = dst_row[t*k+j] (dropped slots: 0);
+    * down: grad_act = grad_y W_d[e];  grad_W_d[e] += grad_y^T act;
+    * SwiGLU: grad_g = grad_act * u * silu'(g);  grad_u = grad_act * silu(g);
+    * gate/up: grad_W_g[e] += grad_g^T x;  grad_W_u[e] += grad_u^T x;
+      grad_x = grad_g W_g[e] + grad_u W_u[e];
+    * permute backward: grad_hidden[t] = sum_j grad_x[dst_row[t*k+j]].
+
+    Returns grad_hidden [T,H], grad_w [T,k] and grad_wgu / grad_wd: dicts
+    expert -> [2I,H] / [H,I] arrays for the experts that received rows."""
+    hidden = np.asarray(hidden, np.float64)
+    grad_out = np.asarray(grad_out, np.float64)
+    T, H = hidden.shape
+    k = top_k_index.shape[1]
+    meta = route_meta(top_k_index, E, G, N)
+    grad_hidden = np.zeros((T, H), np.float64)
+    grad_w = np.zeros((T, k), np.float64)
+    gwgu: Dict[int, np.ndarray] = {}
+    gwd: Dict[int, np.ndarray] = {}
+    for c, (t0, t1) in enumerate(chunk_bounds(T, N)):
+        rows = int(meta["offsets"][c, E]) if t1 > t0 else 0
+        if rows == 0:
+            continue
+        off = meta["offsets"][c]
+        xp = permute(hidden, meta["src_row"][t0 * k:t1 * k], k, rows)
+        dst = np.asarray(meta["dst_row"][t0 * k:t1 * k]).reshape(t1 - t0, k)
+        # recompute y, then the combine backward
+        y = expert_ffn(xp, off, get_expert, I)
+        grad_y = np.zeros((rows, H), np.float64)
+        for j in range(k):
+            keep = np.nonzero(dst[:, j] >= 0)[0]
+            r = dst[keep, j]
+            grad_w[t0 + keep, j] = np.sum(grad_out[t0 + keep] * y[r], axis=1)
+            grad_y[r] = np.asarray(top_k_weights, np.float64)[t0 + keep, j, None] * grad_out[t0 + keep]
+        grad_xp = np.zeros((rows, H), np.float64)
+        for e in range(E):
+            lo, hi = int(off[e]), int(off[e + 1])
+            if hi == lo:
+                continue
+            wgu, wd = get_expert(e)
+            xs = xp[lo:hi]
+            g = xs @ wgu[:I].T
+            u = xs @ wgu[I:2 * I].T
+            act = silu(g) * u
+            gy = grad_y[lo:hi]
+            grad_act = gy @ wd
+            gwd[e] = gwd.get(e, 0.0) + gy.T @ act
+            grad_g = grad_act * u * silu_grad(g)
+            grad_u = grad_act * silu(g)
+            gwgu[e] = gwgu.get(e, 0.0) + np.concatenate([grad_g.T @ xs, grad_u.T @ xs], axis=0)
+            grad_xp[lo:hi] = grad_g @ wgu[:I] + grad_u @ wgu[I:2 * I]
+        for j in range(k):  # ascending slot order
+            keep = np.nonzero(dst[:, j] >= 0)[0]
+            grad_hidden[t0 + keep] += grad_xp[dst[keep, j]]
+    return {"grad_hidden": grad_hidden, "grad_w": grad_w, "grad_wgu": gwgu, "grad_wd": gwd,
+            "meta": meta}
+
+
+def moe_tokens_backward(tokens: Sequence[int], hidden: np.ndarray, top_k_index: np.ndarray,
+                        top_k_weights: np.ndarray, get_expert: ExpertGetter, E: int, I: int,
+                        grad_out: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """grad_hidden and grad_w of single tokens from the plain definition (no
+    permute): grad_w[t,j] = grad_out[t] . FFN_e(x_t) and grad_hidden[t] =
+    sum_j w[t,j] J_e(x_t)^T grad_out[t], with J_e the Jacobian of FFN_e."""
+    tokens = list(tokens)
+    H = hidden.shape[1]
+    k = top_k_index.shape[1]
+    gh = np.zeros((len(tokens), H), np.float64)
+    gw = np.zeros((len(tokens), k), np.float64)
+    for n, t in enumerate(tokens):
+        x = np.asarray(hidden[t], np.float64)
+        go = np.asarray(grad_out[t], np.float64)
+        for j in range(k):
+            e = int(top_k_index[t, j])
+            if not 0 <= e < E:
+                continue
+            wgu, wd = get_expert(e)
+            g = wgu[:I] @ x
+            u = wgu[I:2 * I] @ x
+            gw[n, j] = go @ (wd @ (silu(g) * u))
+            ga = float(top_k_weights[t, j]) * (wd.T @ go)
+            gh[n] += wgu[:I].T @ (ga * u * silu_grad(g)) + wgu[I:2 * I].T @ (ga * silu(g))
+    return gh, gw
+
+
+def expert_weight_grads(e: int, hidden: np.ndarray, top_k_index: np.ndarray,
+                        top_k_weights: np.ndarray, get_expert: ExpertGetter, I: int,
+                        grad_out: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """grad of L with respect to expert e's weights from the plain definition:
+    the sum over every (token, slot) routed to e of the outer products."""
+    wgu, wd = get_expert(e)
+    t_idx, j_idx = np.nonzero(np.asarray(top_k_index) == e)
+    xs = np.asarray(hidden, np.float64)[t_idx]
+    gy = np.asarray(top_k_weights, np.float64)[t_idx, j_idx, None] * \
+        np.asarray(grad_out, np.float64)[t_idx]
+    g = xs @ wgu[:I].T
+    u = xs @ wgu[I:2 * I].T
+    act = silu(g) * u
+    ga = gy @ wd
+    gwd = gy.T @ act
+    gwgu = np.concatenate([(ga * u * silu_grad(g)).T @ xs, (ga * silu(g)).T @ xs], axis=0)
+    return gwgu, gwd
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:

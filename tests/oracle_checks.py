@@ -287,9 +287,103 @@ def check_plain_definition_vs_chunked():
         assert np.allclose(out, direct, rtol=1e-12, atol=1e-12), N
 
 
+# ---------------------------------------------------------------- backward
+def check_silu_grad():
+    """silu'(0) = 1/2 exactly, and central differences of the scalar silu."""
+    assert om.silu_grad(np.array([0.0]))[0] == 0.5
+    for z in (-7.5, -2.0, -0.3, 0.4, 1.0, 3.3, 9.0):
+        h = 1e-6
+        fd = (_scalar_silu(z + h) - _scalar_silu(z - h)) / (2 * h)
+        assert abs(om.silu_grad(np.array([z]))[0] - fd) < 1e-8, z
+
+
+def _bruteforce_loss(x, idx, w, experts, I, grad_out):
+    """sum_t grad_out[t] . out[t] with out from scalar Python loops (no oracle code)."""
+    T, k = idx.shape
+    total = 0.0
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if not 0 <= e < len(experts):
+                continue
+            yr = _bruteforce_ffn_row(list(x[t]), experts[e][0], experts[e][1], I)
+            total += float(w[t, j]) * sum(a * b for a, b in zip(grad_out[t], yr))
+    return total
+
+
+def check_backward_finite_differences():
+    """moe_backward against central differences of the scalar-loop forward, for
+    every input: hidden_states, top_k_weights, w_gate_up and w_down.  The index
+    table has a dropped slot and a token routed twice to one expert."""
+    rng = np.random.default_rng(23)
+    T, H, I, E, k = 5, 4, 3, 3, 2
+    idx = _random_index(rng, T, k, E)
+    idx[1, 1] = -1
+    idx[2, :] = 2
+    w = rng.random((T, k))
+    x = rng.standard_normal((T, H))
+    ex = [[rng.standard_normal((2 * I, H)), rng.standard_normal((H, I))] for _ in range(E)]
+    go = rng.standard_normal((T, H))
+    h = 1e-6
+
+    def fd(arr, pos):
+        old = arr[pos]
+        arr[pos] = old + h
+        lp = _bruteforce_loss(x, idx, w, ex, I, go)
+        arr[pos] = old - h
+        lm = _bruteforce_loss(x, idx, w, ex, I, go)
+        arr[pos] = old
+        return (lp - lm) / (2 * h)
+
+    for N in (1, 2):
+        b = om.moe_backward(x, idx, w, lambda e: (ex[e][0], ex[e][1]), E, I, go, 1, N)
+        for pos in np.ndindex(x.shape):
+            assert abs(b["grad_hidden"][pos] - fd(x, pos)) < 1e-6, ("hidden", N, pos)
+        for pos in np.ndindex(w.shape):
+            want = fd(w, pos)
+            assert abs(b["grad_w"][pos] - want) < 1e-6, ("w", N, pos)
+        for e in range(E):
+            gwgu = b["grad_wgu"].get(e, np.zeros((2 * I, H)))
+            gwd = b["grad_wd"].get(e, np.zeros((H, I)))
+            for pos in np.ndindex(ex[e][0].shape):
+                assert abs(gwgu[pos] - fd(ex[e][0], pos)) < 1e-6, ("wgu", N, e, pos)
+            for pos in np.ndindex(ex[e][1].shape):
+                assert abs(gwd[pos] - fd(ex[e][1], pos)) < 1e-6, ("wd", N, e, pos)
+
+
+def check_backward_views_and_chunking():
+    """The per-token and per-expert backward views equal moe_backward, and the
+    gradient does not depend on the chunk count."""
+    rng = np.random.default_rng(29)
+    T, H, I, E, k = 23, 8, 6, 5, 3
+    idx = _random_index(rng, T, k, E, 0.05)
+    w = rng.random((T, k))
+    x = rng.standard_normal((T, H))
+    ex = [(rng.standard_normal((2 * I, H)) * 0.4, rng.standard_normal((H, I)) * 0.4)
+          for _ in range(E)]
+    get = lambda e: ex[e]  # noqa: E731
+    go = rng.standard_normal((T, H))
+    ref = om.moe_backward(x, idx, w, get, E, I, go, 1, 1)
+    gh, gw = om.moe_tokens_backward(range(T), x, idx, w, get, E, I, go)
+    assert np.allclose(gh, ref["grad_hidden"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(gw, ref["grad_w"], rtol=1e-12, atol=1e-12)
+    for e in range(E):
+        gwgu, gwd = om.expert_weight_grads(e, x, idx, w, get, I, go)
+        assert np.allclose(gwgu, ref["grad_wgu"].get(e, 0 * gwgu), rtol=1e-12, atol=1e-12), e
+        assert np.allclose(gwd, ref["grad_wd"].get(e, 0 * gwd), rtol=1e-12, atol=1e-12), e
+    for N in (2, 4, 30):
+        b = om.moe_backward(x, idx, w, get, E, I, go, 1, N)
+        for key in ("grad_hidden", "grad_w"):
+            assert np.allclose(b[key], ref[key], rtol=1e-12, atol=1e-12), (N, key)
+        for e in ref["grad_wgu"]:
+            assert np.allclose(b["grad_wgu"][e], ref["grad_wgu"][e], rtol=1e-12, atol=1e-12)
+            assert np.allclose(b["grad_wd"][e], ref["grad_wd"][e], rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_chunk_bounds, check_resolve_num_chunks, check_w_pair, check_route_meta_library,
     check_route_meta_bruteforce, check_silu, check_ffn_closed_form, check_ffn_bruteforce,
     check_identity_k1, check_identical_experts_dense, check_weights_linear_and_dropped_slots,
-    check_plain_definition_vs_chunked,
+    check_plain_definition_vs_chunked, check_silu_grad, check_backward_finite_differences,
+    check_backward_views_and_chunking,
 ]

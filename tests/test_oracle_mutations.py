@@ -9,6 +9,7 @@ import oracle_checks
 
 _orig_route_meta = om.route_meta
 _orig_expert_ffn = om.expert_ffn
+_orig_moe_backward = om.moe_backward
 
 
 def _silu_as_sigmoid(z):
@@ -84,7 +85,34 @@ def _w_pair_no_min(T, N, k):
     return 2 * (-(-T // N)) * k
 
 
+def _silu_grad_no_z_term(z):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def _backward_unweighted(hidden, top_k_index, top_k_weights, *a, **kw):
+    return _orig_moe_backward(hidden, top_k_index, np.ones_like(top_k_weights), *a, **kw)
+
+
+def _backward_gate_up_grads_swapped(*a, **kw):
+    b = _orig_moe_backward(*a, **kw)
+    for e, g in b["grad_wgu"].items():
+        half = g.shape[0] // 2
+        b["grad_wgu"][e] = np.concatenate([g[half:], g[:half]], axis=0)
+    return b
+
+
+def _backward_grad_w_slots_reversed(*a, **kw):
+    b = _orig_moe_backward(*a, **kw)
+    b["grad_w"] = b["grad_w"][:, ::-1].copy()
+    return b
+
+
 MUTANTS = {
+    "silu_grad_no_z_term": ("silu_grad", _silu_grad_no_z_term),
+    "backward_unweighted": ("moe_backward", _backward_unweighted),
+    "backward_gate_up_grads_swapped": ("moe_backward", _backward_gate_up_grads_swapped),
+    "backward_grad_w_slots_reversed": ("moe_backward", _backward_grad_w_slots_reversed),
     "silu_as_sigmoid": ("silu", _silu_as_sigmoid),
     "silu_wrong_sign": ("silu", _silu_wrong_sign),
     "ffn_gate_up_swapped": ("expert_ffn", _ffn_gate_up_swapped),
