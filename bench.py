@@ -87,6 +87,35 @@ def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True,
             "workspace_bytes": ws.numel(), "dev_error": int(err.item())}
 
 
+def time_backward(moe, torch, shape, inp, steps, warmup):
+    """Average time of moe_chunked_backward (forward recomputed per chunk pair)."""
+    dt = shape.torch_dtype
+    T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I
+    go = inp["hidden"]  # any [T,H] tensor of the layer dtype serves as the upstream gradient
+    gh = torch.empty((T, H), dtype=dt, device="cuda")
+    gw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    gwgu = torch.empty((E, 2 * I, H), dtype=torch.float32, device="cuda")
+    gwd = torch.empty((E, H, I), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_backward_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+
+    def step():
+        moe.moe_chunked_backward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"], inp["wd"],
+                                 go, gh, gw, gwgu, gwd, ws, None, s0=s0, s1=s1)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del gwgu, gwd
+    return ms, ws.numel()
+
+
 def per_step_times(moe, torch, shape, inp, reps, flush_bytes=0):
     """Median and minimum of single-step times (HIP events around each step).  With
     flush_bytes > 0 a scratch buffer of that size is written before every step,
@@ -280,12 +309,15 @@ def main():
     log("single steps, warm and with L2/MALL flushed")
     warm = per_step_times(moe, torch, shape, inp, 20)
     cold = per_step_times(moe, torch, shape, inp, 20, flush_bytes=1 << 30)
+    log(f"backward N={N}")
+    bwd_ms, bwd_ws = time_backward(moe, torch, shape, inp, max(5, args.steps // 5), 2)
     log("per-kernel timing")
     kt, rows0, e_act0, _ = kernel_times(moe, torch, shape, inp, args.kernel_reps)
     copy_bw = copy_bandwidth(torch)
 
     s = cfg.elem_bytes
     H, I = cfg.H, cfg.I
+    A_valid = int(inp["counts"].sum())
     gu_bytes = rows0 * H * s + e_act0 * 2 * I * H * s + rows0 * I * s
     gu_flops = 2.0 * rows0 * H * 2 * I
     gu_s = kt["gate_up"] * 1e-6
@@ -321,6 +353,13 @@ def main():
         "per_chunk_schedule": {"ms_per_step": run_pc["wall_ms"],
                                "value": cfg.T / (run_pc["wall_ms"] * 1e-3)},
         "single_step": {"warm": warm, "cold": cold},
+        "backward": {"ms_per_step": bwd_ms, "value": cfg.T / (bwd_ms * 1e-3),
+                     "flop_per_step": 18.0 * A_valid * H * I,
+                     "tflops": 18.0 * A_valid * H * I / (bwd_ms * 1e-3) / 1e12,
+                     "workspace_bytes": bwd_ws,
+                     "note": "moe_chunked_backward: forward recomputed per chunk pair, "
+                             "grads of hidden_states, top_k_weights (fp32) and both expert "
+                             "weight tensors (fp32); flop = 18*A*H*I"},
         "workspace_bytes": {"N": main_run["workspace_bytes"], "N1": run1["workspace_bytes"],
                             "slots_model_N": min(N, 2) * -(-cfg.T // N) * cfg.k * (H + I) * s},
         "copy_bandwidth_GBps": copy_bw / 1e9,

@@ -22,7 +22,8 @@ __all__ = [
     "moe_workspace_size", "moe_route_meta", "moe_permute", "moe_expert_gate_up",
     "moe_expert_down", "moe_expert_ffn", "moe_expert_ffn_pair", "moe_expert_gate_up_pair",
     "moe_expert_down_pair", "moe_unpermute_combine", "moe_chunked_forward",
-    "moe_chunked_forward_schedule", "MOE_F32", "MOE_BF16",
+    "moe_chunked_forward_schedule", "moe_backward_workspace_size", "moe_chunked_backward",
+    "moe_unpermute_combine_backward", "moe_permute_backward", "MOE_F32", "MOE_BF16",
     "MOE_SCHEDULE_PAIR_FUSED", "MOE_SCHEDULE_PER_CHUNK", "EXPORTED_SYMBOLS",
 ]
 
@@ -36,7 +37,8 @@ EXPORTED_SYMBOLS = (
     "moe_route_meta_workspace_size", "moe_workspace_size", "moe_route_meta", "moe_permute",
     "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_expert_gate_up_pair",
     "moe_expert_down_pair", "moe_expert_ffn_pair", "moe_unpermute_combine",
-    "moe_chunked_forward", "moe_chunked_forward_schedule",
+    "moe_chunked_forward", "moe_chunked_forward_schedule", "moe_backward_workspace_size",
+    "moe_chunked_backward", "moe_unpermute_combine_backward", "moe_permute_backward",
 )
 
 
@@ -128,6 +130,12 @@ def load_library() -> ctypes.CDLL:
         "moe_chunked_forward_schedule": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P,
                                                         ctypes.c_size_t, _P, _P,
                                                         ctypes.c_int32]),
+        "moe_backward_workspace_size": (ctypes.c_int, [_SP, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_chunked_backward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                _P, _P, ctypes.c_size_t, _P, _P]),
+        "moe_unpermute_combine_backward": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P,
+                                                          _P, _P, _P]),
+        "moe_permute_backward": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -355,3 +363,54 @@ def moe_chunked_forward(shape: moe_shape, hidden_states, top_k_index, top_k_weig
                         w_down, out, ws, dev_error=None, s0=None, s1=None) -> None:
     moe_chunked_forward_schedule(shape, hidden_states, top_k_index, top_k_weights, w_gate_up,
                                  w_down, out, ws, dev_error, s0, s1, _fn="moe_chunked_forward")
+
+
+# ---------------------------------------------------------------- backward
+def moe_backward_workspace_size(shape: moe_shape) -> int:
+    b = ctypes.c_size_t()
+    _check("moe_backward_workspace_size",
+           load_library().moe_backward_workspace_size(ctypes.byref(shape), ctypes.byref(b)))
+    return b.value
+
+
+def moe_chunked_backward(shape: moe_shape, hidden_states, top_k_index, top_k_weights, w_gate_up,
+                         w_down, grad_out, grad_hidden, grad_top_k_weights, grad_w_gate_up,
+                         grad_w_down, ws, dev_error=None, s0=None, s1=None) -> None:
+    dt = shape.torch_dtype
+    T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I  # noqa: E741
+    wp, wn = _ws_ptr(ws, moe_backward_workspace_size(shape))
+    s1i = _stream(s1) if s1 is not None else None
+    _check("moe_chunked_backward", load_library().moe_chunked_backward(
+        ctypes.byref(shape), _ptr(hidden_states, dt, T * H, "hidden_states"),
+        _ptr(top_k_index, torch.int32, T * k, "top_k_index"),
+        _ptr(top_k_weights, torch.float32, T * k, "top_k_weights"),
+        _ptr(w_gate_up, dt, E * 2 * I * H, "w_gate_up"), _ptr(w_down, dt, E * H * I, "w_down"),
+        _ptr(grad_out, dt, T * H, "grad_out"), _ptr(grad_hidden, dt, T * H, "grad_hidden"),
+        _ptr(grad_top_k_weights, torch.float32, T * k, "grad_top_k_weights"),
+        _ptr(grad_w_gate_up, torch.float32, E * 2 * I * H, "grad_w_gate_up"),
+        _ptr(grad_w_down, torch.float32, E * H * I, "grad_w_down"),
+        _ptr(dev_error, torch.int32, 0, "dev_error"), wp, wn, _stream(s0), s1i))
+
+
+def moe_unpermute_combine_backward(shape: moe_shape, chunk: int, grad_out, y, dst_row,
+                                   top_k_weights, grad_y, grad_top_k_weights,
+                                   stream=None) -> None:
+    _, _, rows = _chunk_rows(shape, chunk)
+    dt = shape.torch_dtype
+    T, H, k = shape.T, shape.H, shape.k
+    _check("moe_unpermute_combine_backward", load_library().moe_unpermute_combine_backward(
+        ctypes.byref(shape), chunk, _ptr(grad_out, dt, T * H, "grad_out"),
+        _ptr(y, dt, rows * H, "y"), _ptr(dst_row, torch.int32, T * k, "dst_row"),
+        _ptr(top_k_weights, torch.float32, T * k, "top_k_weights"),
+        _ptr(grad_y, dt, rows * H, "grad_y"),
+        _ptr(grad_top_k_weights, torch.float32, T * k, "grad_top_k_weights"), _stream(stream)))
+
+
+def moe_permute_backward(shape: moe_shape, chunk: int, grad_x_perm, dst_row, grad_hidden,
+                         stream=None) -> None:
+    _, _, rows = _chunk_rows(shape, chunk)
+    dt = shape.torch_dtype
+    _check("moe_permute_backward", load_library().moe_permute_backward(
+        ctypes.byref(shape), chunk, _ptr(grad_x_perm, dt, rows * shape.H, "grad_x_perm"),
+        _ptr(dst_row, torch.int32, shape.T * shape.k, "dst_row"),
+        _ptr(grad_hidden, dt, shape.T * shape.H, "grad_hidden"), _stream(stream)))

@@ -52,6 +52,46 @@ FwdPlan fwd_plan(const Shape& s) {
   return p;
 }
 
+// Layout of the moe_chunked_backward workspace: the forward's metadata, then
+// per slot x_perm and a [rows][H] buffer that holds y, then grad_y, then
+// grad_x_perm; act and the saved g/u (later grad_g/grad_u) of both slots back
+// to back so a pair uses them as joint buffers.
+struct BwdPlan {
+  size_t counts, offsets, splits, src_row, dst_row, dev_err, meta_ws;
+  size_t xp[2], yg[2], act, gu;
+  size_t bytes;
+  int nslots;
+  MetaPlan meta;
+};
+
+BwdPlan bwd_plan(const Shape& s) {
+  BwdPlan p{};
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    size_t at = o;
+    o += align256(n);
+    return at;
+  };
+  p.counts = take((size_t)s.N * s.E * 4);
+  p.offsets = take((size_t)s.N * (s.E + 1) * 4);
+  p.splits = take((size_t)s.N * s.G * 4);
+  p.src_row = take((size_t)s.A * 4);
+  p.dst_row = take((size_t)s.A * 4);
+  p.dev_err = take(4);
+  p.meta = meta_plan(s);
+  p.meta_ws = take(p.meta.bytes);
+  const size_t rows = (size_t)s.Tc * s.k;
+  p.nslots = s.N >= 2 ? 2 : 1;
+  for (int i = 0; i < p.nslots; ++i) {
+    p.xp[i] = take(rows * s.H * s.elem);
+    p.yg[i] = take(rows * s.H * s.elem);
+  }
+  p.act = take(p.nslots * rows * s.I * s.elem);
+  p.gu = take(p.nslots * rows * 2 * s.I * s.elem);
+  p.bytes = o;
+  return p;
+}
+
 // Events that order s0 and s1, per device, cached per host thread.  A wait
 // refers to the event's latest record at the time of the wait call, so one
 // event can be recorded again for every pair.
@@ -105,6 +145,16 @@ moe_status gate_up(const Shape& s, const GroupedIO& io, const void* w, hipStream
 moe_status down(const Shape& s, const GroupedIO& io, const void* w, hipStream_t st) {
   return hip_status(s.dtype == MOE_BF16 ? launch_down_bf16(s, io, w, st)
                                         : launch_down_f32(s, io, w, st));
+}
+
+moe_status dgrad(const Shape& s, const DgradIO& io, hipStream_t st) {
+  return hip_status(s.dtype == MOE_BF16 ? launch_dgrad_bf16(s, io, st)
+                                        : launch_dgrad_f32(s, io, st));
+}
+
+moe_status wgrad(const Shape& s, const WgradIO& io, hipStream_t st) {
+  return hip_status(s.dtype == MOE_BF16 ? launch_wgrad_bf16(s, io, st)
+                                        : launch_wgrad_f32(s, io, st));
 }
 
 // One chunk: A and C are the chunk's own buffers.
@@ -408,6 +458,248 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
   if (!aligned(y, 16) || !aligned(out, 16) || !aligned(dst_row, 4) || !aligned(top_k_weights, 4))
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_combine(s, t0, t1, y, dst_row, top_k_weights, out, stream));
+}
+
+moe_status moe_unpermute_combine_backward(const moe_shape* shape, int32_t chunk,
+                                          const void* grad_out, const void* y,
+                                          const int32_t* dst_row, const float* top_k_weights,
+                                          void* grad_y, float* grad_top_k_weights,
+                                          hipStream_t stream) {
+  Shape s;
+  int t0, t1;
+  moe_status st = resolve_shape(shape, &s);
+  if (st == MOE_OK) st = check_chunk(s, chunk, &t0, &t1);
+  if (st != MOE_OK) return st;
+  if (t1 == t0) return MOE_OK;
+  if (!grad_out || !y || !dst_row || !top_k_weights || !grad_y || !grad_top_k_weights)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_out, 16) || !aligned(y, 16) || !aligned(grad_y, 16) ||
+      !aligned(dst_row, 4) || !aligned(top_k_weights, 4) || !aligned(grad_top_k_weights, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine_backward(s, t0, t1, grad_out, y, dst_row, top_k_weights,
+                                            grad_y, grad_top_k_weights, stream));
+}
+
+moe_status moe_permute_backward(const moe_shape* shape, int32_t chunk, const void* grad_x_perm,
+                                const int32_t* dst_row, void* grad_hidden, hipStream_t stream) {
+  Shape s;
+  int t0, t1;
+  moe_status st = resolve_shape(shape, &s);
+  if (st == MOE_OK) st = check_chunk(s, chunk, &t0, &t1);
+  if (st != MOE_OK) return st;
+  if (t1 == t0) return MOE_OK;
+  if (!grad_x_perm || !dst_row || !grad_hidden) return MOE_ERR_INVALID_ARG;
+  if (!aligned(grad_x_perm, 16) || !aligned(grad_hidden, 16) || !aligned(dst_row, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(s, t0, t1, grad_x_perm, dst_row, nullptr, grad_hidden, stream));
+}
+
+moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes) {
+  Shape s;
+  moe_status st = resolve_shape(shape, &s);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = bwd_plan(s).bytes;
+  return MOE_OK;
+}
+
+moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_states,
+                                const int32_t* top_k_index, const float* top_k_weights,
+                                const void* w_gate_up, const void* w_down, const void* grad_out,
+                                void* grad_hidden, float* grad_top_k_weights,
+                                float* grad_w_gate_up, float* grad_w_down, int32_t* dev_error,
+                                void* ws, size_t ws_bytes, hipStream_t s0, hipStream_t s1) {
+  Shape s;
+  moe_status st = resolve_shape(shape, &s);
+  if (st != MOE_OK) return st;
+  if (!ws || !aligned(ws, 256) || !aligned(dev_error, 4)) return MOE_ERR_INVALID_ARG;
+  const BwdPlan p = bwd_plan(s);
+  if (ws_bytes < p.bytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!w_gate_up || !w_down || !grad_w_gate_up || !grad_w_down) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(grad_w_gate_up, 16) ||
+      !aligned(grad_w_down, 16))
+    return MOE_ERR_INVALID_ARG;
+  if (s.T > 0) {
+    if (!hidden_states || !top_k_index || !top_k_weights || !grad_out || !grad_hidden ||
+        !grad_top_k_weights)
+      return MOE_ERR_INVALID_ARG;
+    if (!aligned(hidden_states, 16) || !aligned(grad_out, 16) || !aligned(grad_hidden, 16) ||
+        !aligned(top_k_index, 4) || !aligned(top_k_weights, 4) ||
+        !aligned(grad_top_k_weights, 4))
+      return MOE_ERR_INVALID_ARG;
+  }
+  char* w = (char*)ws;
+  int32_t* counts = (int32_t*)(w + p.counts);
+  int32_t* offsets = (int32_t*)(w + p.offsets);
+  int32_t* splits = (int32_t*)(w + p.splits);
+  int32_t* src_row = (int32_t*)(w + p.src_row);
+  int32_t* dst_row = (int32_t*)(w + p.dst_row);
+  int32_t* err = dev_error ? dev_error : (int32_t*)(w + p.dev_err);
+  hipError_t he = launch_route_meta(s, top_k_index, counts, offsets, splits, src_row, dst_row,
+                                    err, w + p.meta_ws, s0);
+  if (he != hipSuccess) return MOE_ERR_HIP;
+
+  const bool two = (s1 != nullptr && s1 != s0 && s.N >= 2);
+  hipEvent_t ev[kEvents] = {};
+  if (two) {
+    he = thread_events(ev);
+    if (he == hipSuccess) he = join(s1, s0, ev[0]);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+  }
+  bool used_s1 = false, first = true;
+  auto chunk_rows = [&](int c, int* t0, int* t1) {
+    *t0 = *t1 = 0;
+    if (c < s.N) chunk_tokens(s, c, t0, t1);
+    return (int64_t)(*t1 - *t0) * s.k;
+  };
+  // Pair (c, c+1): permutes (c on s0, c+1 on s1); on s0: gate_up (act and the
+  // saved g/u), down (y), then after the combine backwards (c on s0, c+1 on s1):
+  // dgrad of down with the SwiGLU backward (grad_g/grad_u over g/u), the W_d
+  // wgrad, the gate/up dgrad (grad_x over y's buffer), the W_gu wgrad; then the
+  // permute backwards (c on s0, c+1 on s1).
+  for (int c = 0; c < s.N; c += 2) {
+    int t0, t1, u0, u1;
+    const int64_t rows0 = chunk_rows(c, &t0, &t1), rows1 = chunk_rows(c + 1, &u0, &u1);
+    if (rows0 + rows1 == 0) continue;
+    hipStream_t st1 = two ? s1 : s0;
+    void* xp0 = w + p.xp[0];
+    void* xp1 = p.nslots > 1 ? w + p.xp[1] : nullptr;
+    void* yg0 = w + p.yg[0];
+    void* yg1 = p.nslots > 1 ? w + p.yg[1] : nullptr;
+    const int32_t* off0 = offsets + (size_t)c * (s.E + 1);
+    const int32_t* off1 = rows1 > 0 ? off0 + (s.E + 1) : nullptr;
+    he = launch_permute(s, t0, t1, hidden_states, dst_row, xp0, s0);
+    if (he == hipSuccess && rows1 > 0) he = launch_permute(s, u0, u1, hidden_states, dst_row, xp1, st1);
+    if (he == hipSuccess && two && rows1 > 0) {
+      used_s1 = true;
+      he = join(s0, s1, ev[1]);
+    }
+    if (he != hipSuccess) return MOE_ERR_HIP;
+    // forward recompute: act + saved g/u, then y
+    GroupedIO io{};
+    io.off[0] = off0;
+    io.off[1] = off1;
+    io.rows_bound = rows0 + rows1;
+    io.a[0] = xp0;
+    io.a[1] = xp1;
+    io.a_split = true;
+    io.c[0] = w + p.act;
+    io.gu = w + p.gu;
+    st = gate_up(s, io, w_gate_up, s0);
+    if (st != MOE_OK) return st;
+    io.gu = nullptr;
+    io.a[0] = w + p.act;
+    io.a[1] = nullptr;
+    io.a_split = false;
+    io.c[0] = yg0;
+    io.c[1] = yg1;
+    io.c_split = true;
+    st = down(s, io, w_down, s0);
+    if (st != MOE_OK) return st;
+    if (two && rows1 > 0) {
+      he = join(s1, s0, ev[2]);
+      if (he != hipSuccess) return MOE_ERR_HIP;
+    }
+    // combine backward: grad_w rows of the pair's tokens, grad_y over y
+    he = launch_combine_backward(s, t0, t1, grad_out, yg0, dst_row, top_k_weights, yg0,
+                                 grad_top_k_weights, s0);
+    if (he == hipSuccess && rows1 > 0)
+      he = launch_combine_backward(s, u0, u1, grad_out, yg1, dst_row, top_k_weights, yg1,
+                                   grad_top_k_weights, st1);
+    if (he == hipSuccess && two && rows1 > 0) he = join(s0, s1, ev[1]);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+    // dgrad of down with the SwiGLU backward: g/u -> grad_g/grad_u
+    DgradIO dd{};
+    dd.a[0] = yg0;
+    dd.a[1] = yg1;
+    dd.a_split = true;
+    dd.B = w_down;
+    dd.K = s.H;
+    dd.N = s.I;
+    dd.gu = w + p.gu;
+    dd.off[0] = off0;
+    dd.off[1] = off1;
+    dd.rows_bound = rows0 + rows1;
+    st = dgrad(s, dd, s0);
+    if (st != MOE_OK) return st;
+    // W_d wgrad reads grad_y and act
+    WgradIO wd{};
+    wd.a[0] = yg0;
+    wd.a[1] = yg1;
+    wd.a_split = true;
+    wd.b[0] = w + p.act;
+    wd.C = grad_w_down;
+    wd.M = s.H;
+    wd.N = s.I;
+    wd.accumulate = first ? 0 : 1;
+    wd.off[0] = off0;
+    wd.off[1] = off1;
+    st = wgrad(s, wd, s0);
+    if (st != MOE_OK) return st;
+    // gate/up dgrad: grad_x over y's (now free) buffer
+    DgradIO dg{};
+    dg.a[0] = w + p.gu;
+    dg.a_split = false;
+    dg.B = w_gate_up;
+    dg.K = 2 * s.I;
+    dg.N = s.H;
+    dg.c[0] = yg0;
+    dg.c[1] = yg1;
+    dg.c_split = true;
+    dg.off[0] = off0;
+    dg.off[1] = off1;
+    dg.rows_bound = rows0 + rows1;
+    st = dgrad(s, dg, s0);
+    if (st != MOE_OK) return st;
+    // W_gu wgrad reads grad_g/grad_u and x_perm
+    WgradIO wg{};
+    wg.a[0] = w + p.gu;
+    wg.a_split = false;
+    wg.b[0] = xp0;
+    wg.b[1] = xp1;
+    wg.b_split = true;
+    wg.C = grad_w_gate_up;
+    wg.M = 2 * s.I;
+    wg.N = s.H;
+    wg.accumulate = first ? 0 : 1;
+    wg.off[0] = off0;
+    wg.off[1] = off1;
+    st = wgrad(s, wg, s0);
+    if (st != MOE_OK) return st;
+    first = false;
+    if (two && rows1 > 0) {
+      he = join(s1, s0, ev[2]);
+      if (he != hipSuccess) return MOE_ERR_HIP;
+    }
+    // permute backward: grad_hidden[t] = sum_j grad_x[dst_row[t*k+j]]
+    he = launch_combine(s, t0, t1, yg0, dst_row, nullptr, grad_hidden, s0);
+    if (he == hipSuccess && rows1 > 0)
+      he = launch_combine(s, u0, u1, yg1, dst_row, nullptr, grad_hidden, st1);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (first) {
+    // no rows at all: the weight gradients are zero
+    WgradIO z{};
+    z.a[0] = w + p.act;
+    z.b[0] = w + p.act;
+    z.off[0] = offsets;
+    z.accumulate = 0;
+    z.C = grad_w_down;
+    z.M = s.H;
+    z.N = s.I;
+    st = wgrad(s, z, s0);
+    if (st != MOE_OK) return st;
+    z.C = grad_w_gate_up;
+    z.M = 2 * s.I;
+    z.N = s.H;
+    st = wgrad(s, z, s0);
+    if (st != MOE_OK) return st;
+  }
+  if (two && used_s1) {
+    he = join(s0, s1, ev[1]);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
 }
 
 moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidden_states,

@@ -74,6 +74,7 @@ struct GemmArgs {
   int E, K, I, ncols, n_tiles;
   int lo_rows, hi_rows;       // experts handled by this launch: lo_rows <= rows < hi_rows
   int64_t b_expert_stride;    // elements per expert in B
+  uint16_t* gu;               // gate_up, optional: g and u of each row, joint [rows][2I]
 };
 
 // Address of virtual row v of the tile's expert on one side of the product.
@@ -220,6 +221,15 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
           const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
           crow[col] = to_bf16_bits(g / (1.0f + expf(-g)) * u);
         }
+        if (a.gu) {  // the backward's saved pre-activations
+          uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const int col = nt * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
+            gr[col] = to_bf16_bits(acc[i][j][q]);
+            gr[a.I + col] = to_bf16_bits(acc[i][j + FN / 2][q]);
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -358,6 +368,7 @@ hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void*
   a.off1 = io.off[1];
   a.a_split = io.a_split && io.off[1];
   a.c_split = io.c_split && io.off[1];
+  a.gu = gate_up ? (uint16_t*)io.gu : nullptr;
   a.B = (const uint16_t*)B;
   a.E = s.E;
   a.I = s.I;

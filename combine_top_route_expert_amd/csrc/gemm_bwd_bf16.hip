@@ -1,0 +1,454 @@
+// Backward grouped GEMMs on gfx950 bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// Gradient of the expert computation of the MindSpeed Chunk MoE article (core
+// principle / timing-diagram sections; SwiGLU reading), chunk pair by chunk
+// pair with the forward recomputed (the guide's recompute option):
+//   dgrad down  : grad_act[r] = grad_y[r] . W_d[e]        ([rows][H] x [H][I])
+//                 fused with the SwiGLU backward: grad_g = grad_act u silu'(g),
+//                 grad_u = grad_act silu(g), written over the saved g, u
+//   dgrad gate/up: grad_x[r] = grad_gu[r] . W_gu[e]      ([rows][2I] x [2I][H])
+//   wgrad       : grad_W[e] (+)= sum over e's rows v of A[v]^T B[v]
+//                 (W_d: A = grad_y, B = act;  W_gu: A = grad_gu, B = x_perm)
+//
+// The dgrad B operand (weights [K][N]) and both wgrad operands ([rows][M],
+// [rows][N], the reduction running over rows) are stored with the reduction
+// index outermost.  Stages are copied global -> LDS row by row with the
+// direct-to-LDS load, and the MFMA fragments (8 consecutive K values of one
+// column per lane) are read with ds_read_b64_tr_b16: within each group of 16
+// lanes, output lane i element j comes from source lane 4j + i/4, element i%4
+// (measured), so a source lane that reads 4 consecutive columns of one K row
+// delivers a 4 (K) x 16 (column) block already transposed.  The 16-byte chunk c
+// of LDS row k sits at slot c ^ 4(k mod 4), which spreads the 4 rows x 4 chunks
+// a 32-lane phase reads over 16 distinct bank groups.
+//
+// Grouping and XCD placement follow the forward kernels (MTileMap, xcd_tile);
+// the wgrad tiles are numbered (expert, m-tile) and its K loop runs over the
+// expert's rows of both chunks; rows past the expert's block are loaded from a
+// clamped row and zeroed in the A fragment.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int BK = 64;
+constexpr int wait_vm(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// One operand side of a grouped product: rows of expert e are its chunk-0 rows
+// then its chunk-1 rows, either in two buffers (split) or grouped in one (joint).
+struct Side {
+  const uint16_t* p[2];
+  int split;
+  int64_t ld;  // elements per row
+};
+
+__device__ __forceinline__ const uint16_t* side_row(const Side& s, const TileRows& tr, int v) {
+  if (s.split) {
+    int part;
+    const int r = tr.split_row(v, &part);
+    return (part ? s.p[1] : s.p[0]) + (int64_t)r * s.ld;
+  }
+  return s.p[0] + (int64_t)tr.joint_row(v) * s.ld;
+}
+
+// ---- LDS layouts --------------------------------------------------------------
+// K-contiguous rows (dgrad A): BM rows x 128 bytes per stage, chunk c of row r at
+// slot c ^ ((r >> 1) & 7) (same as the forward kernels).
+__device__ __forceinline__ int kfrag_offset(int lane, int kk) {
+  const int r = lane & 31;
+  const int chunk = 2 * kk + (lane >> 5);
+  return r * 128 + ((chunk ^ ((r >> 1) & 7)) << 4);
+}
+
+// Column-contiguous rows (K outermost): BK rows x (C * 2) bytes per stage.
+template <int C>
+struct MnGeom {
+  static_assert(C == 128 || C == 256, "column tile");
+  static constexpr int ROW_BYTES = C * 2;
+  static constexpr int SLOTS = ROW_BYTES / 16;      // 16-byte chunks per row
+  static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
+  static constexpr int STAGE_BYTES = BK * ROW_BYTES;
+  static __device__ __forceinline__ int swz(int k) { return 4 * (k & 3); }
+  // Fragment of the 32 columns starting at cb, K step kk (16 rows), half h (rows
+  // 4h..4h+3 of the lane's 8): byte offset of this lane's ds_read_b64_tr_b16.
+  static __device__ __forceinline__ int tr_offset(int lane, int cb, int kk, int h) {
+    const int g = lane >> 4, s = lane & 15;
+    const int k = 16 * kk + 8 * (g >> 1) + 4 * h + (s >> 2);
+    const int col = cb + 16 * (g & 1) + 4 * (s & 3);
+    return k * ROW_BYTES + (((col >> 3) ^ swz(k)) << 4) + ((col & 7) << 1);
+  }
+};
+
+__device__ __forceinline__ bf16x8 tr_frag(const char* stage, int off0, int off1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
+  const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- dgrad ------------------------------------------------------------------------
+enum DgradEpi { kDgradPlain = 0, kDgradSwiglu = 1 };
+
+struct DgradArgs {
+  Side a;                    // [rows][K], K contiguous
+  const uint16_t* B;         // [E][K][N]
+  int64_t b_expert_stride;
+  uint16_t* C[2];            // plain: [rows][N] (split when c_split)
+  int c_split;
+  uint16_t* gu;              // swiglu: [rows][2I] joint, g then u; overwritten with grads
+  const int32_t* off0;
+  const int32_t* off1;
+  int E, K, N, I, n_tiles;
+};
+
+template <int kEpi, int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradArgs a) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  using GB = MnGeom<BN>;
+  constexpr int A_BYTES = BM * 128;
+  constexpr int STAGE = A_BYTES + GB::STAGE_BYTES;
+  constexpr int LA = BM / 8 / NW;                        // 1 KB A blocks per wave
+  constexpr int LB = GB::STAGE_BYTES / 1024 / NW;        // 1 KB B blocks per wave
+  static_assert(LA * 8 * NW == BM && LB * 1024 * NW == GB::STAGE_BYTES, "blocks per wave");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  MTileMap tm;
+  tm.build(a.off0, a.off1, a.E, BM);
+  int mt, nt;
+  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
+
+  // A: lane l of block b holds tile row 8b + l/8, 16-byte slot l % 8
+  const char* a_src[LA];
+  int live_a = 0;
+#pragma unroll
+  for (int t = 0; t < LA; ++t) {
+    const int row = (wave * LA + t) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    const int r = row < tr.rows ? row : tr.rows - 1;
+    a_src[t] = (const char*)(side_row(a.a, tr, tr.v0 + r) + chunk * 8);
+    live_a += (wave * LA + t) * 8 < tr.rows ? 1 : 0;
+  }
+  // B: lane l of block b holds K row ROWS_PER_KB*b + l/SLOTS, slot l % SLOTS
+  const uint16_t* Be = a.B + (int64_t)tr.e * a.b_expert_stride;
+  const char* b_src[LB];
+#pragma unroll
+  for (int t = 0; t < LB; ++t) {
+    const int k = (wave * LB + t) * GB::ROWS_PER_KB + lane / GB::SLOTS;
+    const int slot = lane % GB::SLOTS;
+    int col = nt * BN + 8 * (slot ^ GB::swz(k));
+    if (col > a.N - 8) col = a.N - 8;
+    b_src[t] = (const char*)(Be + (int64_t)k * a.N + col);
+  }
+  auto issue = [&](int kt, int buf) {
+    char* base = smem + buf * STAGE;
+#pragma unroll
+    for (int t = 0; t < LA; ++t)
+      if (t < live_a)
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + (int64_t)kt * 128),
+                                         (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < LB; ++t)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + (int64_t)kt * BK * a.N * 2),
+                                       (lds_void*)(base + A_BYTES + (wave * LB + t) * 1024), 16,
+                                       0, 0);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  const int KT = a.K / BK;
+  const bool rows_live = wm * WM < tr.rows;
+  issue(0, 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
+    const char* sa = smem + (kt & 1) * STAGE;
+    const char* sb = sa + A_BYTES;
+    if (rows_live) {
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int fo = kfrag_offset(lane, kk);
+        bf16x8 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * 128 + fo);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int cb = wn * WN + j * 32;
+          bfr[j] = tr_frag(sb, GB::tr_offset(lane, cb, kk, 0), GB::tr_offset(lane, cb, kk, 1));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+
+  // epilogue: lane l holds column l % 32 of rows 8(q/4) + 4(l/32) + q%4 of each block
+  const int rbase = wm * WM + 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+      if (row >= tr.rows) continue;
+      const int v = tr.v0 + row;
+      if constexpr (kEpi == kDgradSwiglu) {
+        uint16_t* gr = a.gu + (int64_t)tr.joint_row(v) * (2 * a.I);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
+          if (col >= a.N) continue;
+          const float ga = acc[i][j][q];
+          const float g = bf16_to_f32(gr[col]), u = bf16_to_f32(gr[a.I + col]);
+          const float s = 1.0f / (1.0f + expf(-g));
+          gr[col] = to_bf16_bits(ga * u * (s + g * s * (1.0f - s)));
+          gr[a.I + col] = to_bf16_bits(ga * (g * s));
+        }
+      } else {
+        uint16_t* cr;
+        if (a.c_split) {
+          int part;
+          const int r = tr.split_row(v, &part);
+          cr = a.C[part] + (int64_t)r * a.N;
+        } else {
+          cr = a.C[0] + (int64_t)tr.joint_row(v) * a.N;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
+          if (col < a.N) cr[col] = to_bf16_bits(acc[i][j][q]);
+        }
+      }
+    }
+}
+
+// ---- wgrad ------------------------------------------------------------------------
+struct WgradArgs {
+  Side a;            // [rows][M]
+  Side b;            // [rows][N]
+  float* C;          // [E][M][N]
+  const int32_t* off0;
+  const int32_t* off1;
+  int E, M, N, m_tiles, n_tiles;
+  int accumulate;    // 0: C = sum (experts without rows get zeros); 1: C += sum
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradArgs a) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  using GA = MnGeom<BM>;
+  using GB = MnGeom<BN>;
+  constexpr int STAGE = GA::STAGE_BYTES + GB::STAGE_BYTES;
+  constexpr int LA = GA::STAGE_BYTES / 1024 / NW, LB = GB::STAGE_BYTES / 1024 / NW;
+  static_assert(LA * 1024 * NW == GA::STAGE_BYTES && LB * 1024 * NW == GB::STAGE_BYTES,
+                "blocks per wave");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  int emt, nt;
+  if (!xcd_tile(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
+  const int e = emt / a.m_tiles, mt = emt - e * a.m_tiles;
+  TileRows tr;
+  tr.e = e;
+  tr.v0 = 0;
+  tr.lo0 = a.off0[e];
+  tr.n0 = a.off0[e + 1] - tr.lo0;
+  tr.lo1 = a.off1 ? a.off1[e] : 0;
+  const int n1 = a.off1 ? a.off1[e + 1] - tr.lo1 : 0;
+  const int rows = tr.n0 + n1;
+  tr.rows = rows;
+  if (rows == 0 && a.accumulate) return;
+
+  // per lane: the K row (within a stage) and column of each 1 KB block it loads
+  int a_k[LA], a_col[LA], b_k[LB], b_col[LB];
+#pragma unroll
+  for (int t = 0; t < LA; ++t) {
+    a_k[t] = (wave * LA + t) * GA::ROWS_PER_KB + lane / GA::SLOTS;
+    int col = mt * BM + 8 * ((lane % GA::SLOTS) ^ GA::swz(a_k[t]));
+    a_col[t] = col > a.M - 8 ? a.M - 8 : col;
+  }
+#pragma unroll
+  for (int t = 0; t < LB; ++t) {
+    b_k[t] = (wave * LB + t) * GB::ROWS_PER_KB + lane / GB::SLOTS;
+    int col = nt * BN + 8 * ((lane % GB::SLOTS) ^ GB::swz(b_k[t]));
+    b_col[t] = col > a.N - 8 ? a.N - 8 : col;
+  }
+  auto issue = [&](int kt, int buf) {
+    char* base = smem + buf * STAGE;
+#pragma unroll
+    for (int t = 0; t < LA; ++t) {
+      int v = kt * BK + a_k[t];
+      v = v < rows ? v : rows - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(side_row(a.a, tr, v) + a_col[t]),
+                                       (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < LB; ++t) {
+      int v = kt * BK + b_k[t];
+      v = v < rows ? v : rows - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(side_row(a.b, tr, v) + b_col[t]),
+                                       (lds_void*)(base + GA::STAGE_BYTES + (wave * LB + t) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  const int KT = (rows + BK - 1) / BK;
+  if (KT > 0) issue(0, 0);
+  const int g = lane >> 4;
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
+    const char* sa = smem + (kt & 1) * STAGE;
+    const char* sb = sa + GA::STAGE_BYTES;
+    const int kvalid = rows - kt * BK;  // K rows of this stage that exist
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      if (16 * kk >= kvalid) break;
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int cb = wm * WM + i * 32;
+        af[i] = tr_frag(sa, GA::tr_offset(lane, cb, kk, 0), GA::tr_offset(lane, cb, kk, 1));
+      }
+      if (16 * kk + 16 > kvalid) {
+        // element j of half h is K row 16kk + 8(g/2) + 4h + j: zero rows past the block
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            if (16 * kk + 8 * (g >> 1) + x >= kvalid) af[i][x] = (__bf16)0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cb = wn * WN + j * 32;
+        bfr[j] = tr_frag(sb, GB::tr_offset(lane, cb, kk, 0), GB::tr_offset(lane, cb, kk, 1));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+
+  float* Ce = a.C + (int64_t)e * a.M * a.N;
+  const int rbase = wm * WM + 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = mt * BM + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+      if (m >= a.M) continue;
+      float* cr = Ce + (int64_t)m * a.N;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = nt * BN + wn * WN + j * 32 + (lane & 31);
+        if (n >= a.N) continue;
+        cr[n] = a.accumulate ? cr[n] + acc[i][j][q] : acc[i][j][q];
+      }
+    }
+}
+
+int64_t grid_of(int64_t m_bound, int n_tiles) { return xcd_grid(m_bound, n_tiles); }
+
+}  // namespace
+
+hipError_t launch_dgrad_bf16(const Shape& s, const DgradIO& io, hipStream_t st) {
+  if (io.rows_bound <= 0) return hipSuccess;
+  DgradArgs a{};
+  a.a.p[0] = (const uint16_t*)io.a[0];
+  a.a.p[1] = (const uint16_t*)(io.a_split ? io.a[1] : io.a[0]);
+  a.a.split = io.a_split && io.off[1];
+  a.a.ld = io.K;
+  a.B = (const uint16_t*)io.B;
+  a.b_expert_stride = (int64_t)io.K * io.N;
+  a.C[0] = (uint16_t*)io.c[0];
+  a.C[1] = (uint16_t*)(io.c_split ? io.c[1] : io.c[0]);
+  a.c_split = io.c_split && io.off[1];
+  a.gu = (uint16_t*)io.gu;
+  a.off0 = io.off[0];
+  a.off1 = io.off[1];
+  a.E = s.E;
+  a.K = io.K;
+  a.N = io.N;
+  a.I = s.I;
+  constexpr int BM = 256, BN = 256;
+  a.n_tiles = (io.N + BN - 1) / BN;
+  const int64_t grid = grid_of(m_tiles_bound(io.rows_bound, s.E, BM), a.n_tiles);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (io.gu)
+    hipLaunchKernelGGL((dgrad_gemm_bf16<kDgradSwiglu, BM, BN, 2, 4>), dim3((unsigned)grid),
+                       dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((dgrad_gemm_bf16<kDgradPlain, BM, BN, 2, 4>), dim3((unsigned)grid),
+                       dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16(const Shape& s, const WgradIO& io, hipStream_t st) {
+  WgradArgs a{};
+  a.a.p[0] = (const uint16_t*)io.a[0];
+  a.a.p[1] = (const uint16_t*)(io.a_split ? io.a[1] : io.a[0]);
+  a.a.split = io.a_split && io.off[1];
+  a.a.ld = io.M;
+  a.b.p[0] = (const uint16_t*)io.b[0];
+  a.b.p[1] = (const uint16_t*)(io.b_split ? io.b[1] : io.b[0]);
+  a.b.split = io.b_split && io.off[1];
+  a.b.ld = io.N;
+  a.C = io.C;
+  a.off0 = io.off[0];
+  a.off1 = io.off[1];
+  a.E = s.E;
+  a.M = io.M;
+  a.N = io.N;
+  a.accumulate = io.accumulate;
+  constexpr int BM = 256, BN = 256;
+  a.m_tiles = (io.M + BM - 1) / BM;
+  a.n_tiles = (io.N + BN - 1) / BN;
+  const int64_t grid = grid_of((int64_t)s.E * a.m_tiles, a.n_tiles);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((wgrad_gemm_bf16<BM, BN, 2, 4>), dim3((unsigned)grid), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

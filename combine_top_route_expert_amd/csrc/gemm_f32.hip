@@ -28,6 +28,7 @@ struct GemmArgs {
   int a_split, c_split;
   int E, K, I, ncols, n_tiles;
   int64_t b_expert_stride;
+  float* gu;              // gate_up, optional: g and u of each row, joint [rows][2I]
 };
 
 // Address of virtual row v of the tile's expert on one side of the product.
@@ -123,6 +124,11 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_f32(GemmArgs a) {
         if (i < a.I) {
           const float g = acc[r][q], u = acc[r][q + 2];
           crow[i] = g / (1.0f + expf(-g)) * u;
+          if (a.gu) {  // the backward's saved pre-activations
+            float* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
+            gr[i] = g;
+            gr[a.I + i] = u;
+          }
         }
       }
     } else {
@@ -147,6 +153,7 @@ hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void*
   a.off1 = io.off[1];
   a.a_split = io.a_split && io.off[1];
   a.c_split = io.c_split && io.off[1];
+  a.gu = gate_up ? (float*)io.gu : nullptr;
   a.B = (const float*)B;
   a.E = s.E;
   a.I = s.I;

@@ -47,6 +47,7 @@ hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts
 // ---- permute / combine (permute_combine.hip) --------------------------------
 hipError_t launch_permute(const Shape& s, int t0, int t1, const void* hidden,
                           const int32_t* dst_row, void* x_perm, hipStream_t st);
+// w may be null: unit weights (the permute backward, a gather-sum over k rows).
 hipError_t launch_combine(const Shape& s, int t0, int t1, const void* y,
                           const int32_t* dst_row, const float* w, void* out, hipStream_t st);
 
@@ -65,7 +66,39 @@ struct GroupedIO {
   const int32_t* off[2]; // E + 1 chunk-local offsets of each chunk; off[1] may be null
   bool a_split, c_split;
   int64_t rows_bound;    // total rows of the launch (host-known bound)
+  void* gu = nullptr;    // gate_up only, optional: joint [rows][2I] copy of g and u
 };
+
+// Backward products (gemm_bwd_bf16.hip, gemm_bwd_f32.hip).  Rows follow the
+// GroupedIO rules (split or joint sides, one chunk or a pair).
+struct DgradIO {         // C[r] = A[r] . B[e]   with B[e] stored [K][N]
+  const void* a[2];      // [rows][K]
+  bool a_split;
+  const void* B;         // [E][K][N]
+  int K, N;
+  void* c[2];            // [rows][N] (plain epilogue)
+  bool c_split;
+  void* gu;              // SwiGLU epilogue (N = I): joint [rows][2I] g, u -> grad_g, grad_u
+  const int32_t* off[2];
+  int64_t rows_bound;
+};
+struct WgradIO {         // C[e] (+)= sum over e's rows v of A[v]^T B[v]
+  const void* a[2];      // [rows][M]
+  bool a_split;
+  const void* b[2];      // [rows][N]
+  bool b_split;
+  float* C;              // [E][M][N]
+  int M, N;
+  int accumulate;        // 0: overwrite (experts without rows get zeros), 1: add
+  const int32_t* off[2];
+};
+hipError_t launch_dgrad_bf16(const Shape& s, const DgradIO& io, hipStream_t st);
+hipError_t launch_wgrad_bf16(const Shape& s, const WgradIO& io, hipStream_t st);
+hipError_t launch_dgrad_f32(const Shape& s, const DgradIO& io, hipStream_t st);
+hipError_t launch_wgrad_f32(const Shape& s, const WgradIO& io, hipStream_t st);
+hipError_t launch_combine_backward(const Shape& s, int t0, int t1, const void* grad_out,
+                                   const void* y, const int32_t* dst_row, const float* w,
+                                   void* grad_y, float* grad_w, hipStream_t st);
 hipError_t launch_gate_up_bf16(const Shape& s, const GroupedIO& io, const void* w_gate_up,
                                hipStream_t st);
 hipError_t launch_down_bf16(const Shape& s, const GroupedIO& io, const void* w_down,

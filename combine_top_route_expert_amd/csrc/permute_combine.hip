@@ -14,6 +14,8 @@
 //  * combine reads the token's k expert-output rows, accumulates
 //    w[t,j] * y[row_j] in fp32 in ascending j, and rounds once on the store.
 // Both are HBM-bound: permute moves T*H*s + A*H*s bytes, combine A*H*s + T*H*s.
+// The backward reuses combine_rows with unit weights (the permute's backward is
+// a gather-sum of a token's k rows) and adds combine_backward below.
 #include "moe_internal.h"
 
 namespace moe {
@@ -85,7 +87,7 @@ combine_rows(const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
   if (t >= t1) return;
   // the token's k rows and weights, one slot per lane, fetched in one round trip
   const int my_row = lane < k ? dst_row[(size_t)t * k + lane] : -1;
-  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
+  const float my_w = lane < k ? (w ? w[(size_t)t * k + lane] : 1.0f) : 0.0f;
   for (int v0 = 0; v0 < nvec; v0 += 64 * kVecPerLane) {
     float acc[kVecPerLane][kEl];
 #pragma unroll
@@ -148,7 +150,83 @@ combine_rows(const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
   }
 }
 
+// Combine backward, one wave per token: for each kept slot j with row r,
+// grad_w[t,j] = grad_out[t] . y[r] (fp32, each lane's partial in ascending
+// vector order, then a fixed butterfly) and grad_y[r] = w[t,j] grad_out[t]
+// (rounded once).  grad_y may alias y: row r is read, then overwritten, by the
+// same wave.  Dropped slots get grad_w = 0.
+template <bool kBf16>
+__global__ void __launch_bounds__(64 * kWavesPerBlock)
+combine_backward(const u32x4* __restrict__ grad_out, const u32x4* y, const int32_t* __restrict__ dst_row,
+                 const float* __restrict__ w, u32x4* grad_y, float* __restrict__ grad_w, int t0,
+                 int t1, int k, int nvec) {
+  constexpr int kEl = kBf16 ? 8 : 4;
+  const int lane = threadIdx.x & 63;
+  const int t = t0 + blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= t1) return;
+  const int my_row = lane < k ? dst_row[(size_t)t * k + lane] : -1;
+  const float my_w = lane < k ? w[(size_t)t * k + lane] : 0.0f;
+  const u32x4* go = grad_out + (size_t)t * nvec;
+  for (int j = 0; j < k; ++j) {
+    const int r = __shfl(my_row, j);
+    const float wj = __shfl(my_w, j);
+    if (r < 0) {
+      if (lane == 0) grad_w[(size_t)t * k + j] = 0.0f;
+      continue;
+    }
+    const u32x4* yr = y + (size_t)r * nvec;
+    u32x4* gy = grad_y + (size_t)r * nvec;
+    float dot = 0.0f;
+    for (int v = lane; v < nvec; v += 64) {
+      const u32x4 gq = go[v], yq = yr[v];
+      float gf[kEl], yf[kEl];
+      if constexpr (kBf16) {
+        unpack_bf16x8(gq, gf);
+        unpack_bf16x8(yq, yf);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gf[q] = __uint_as_float(gq[q]);
+          yf[q] = __uint_as_float(yq[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kEl; ++q) {
+        dot = __builtin_fmaf(gf[q], yf[q], dot);
+        gf[q] *= wj;
+      }
+      if constexpr (kBf16) {
+        gy[v] = pack_bf16x8(gf);
+      } else {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(gf[q]);
+        gy[v] = o;
+      }
+    }
+    for (int d = 32; d > 0; d >>= 1) dot += __shfl_xor(dot, d);
+    if (lane == 0) grad_w[(size_t)t * k + j] = dot;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_backward(const Shape& s, int t0, int t1, const void* grad_out,
+                                   const void* y, const int32_t* dst_row, const float* w,
+                                   void* grad_y, float* grad_w, hipStream_t st) {
+  if (t1 <= t0) return hipSuccess;
+  const int nvec = (int)((int64_t)s.H * s.elem / 16);
+  const unsigned blocks = (unsigned)((t1 - t0 + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (s.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_backward<true>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
+                       (const u32x4*)grad_out, (const u32x4*)y, dst_row, w, (u32x4*)grad_y,
+                       grad_w, t0, t1, s.k, nvec);
+  else
+    hipLaunchKernelGGL(combine_backward<false>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
+                       (const u32x4*)grad_out, (const u32x4*)y, dst_row, w, (u32x4*)grad_y,
+                       grad_w, t0, t1, s.k, nvec);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const Shape& s, int t0, int t1, const void* hidden,
                           const int32_t* dst_row, void* x_perm, hipStream_t st) {

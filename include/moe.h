@@ -254,6 +254,69 @@ moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states
                                int32_t* dev_error, void* ws, size_t ws_bytes, hipStream_t s0,
                                hipStream_t s1);
 
+/* ---------------------------------------------------------------------------
+ * Backward of the same layer (gradient of L = sum(grad_out * out)), chunk pair
+ * by chunk pair with each chunk's forward recomputed instead of stored (the
+ * MindSpeed Chunk MoE guide's recompute option, "操作指南" step 3; the
+ * backward mirrors the forward timing diagram chunk by chunk).
+ *
+ * Per pair: the permutes, the gate/up GEMM (act plus a saved copy of g and u)
+ * and the down GEMM (y) are recomputed; then
+ *   grad_top_k_weights[t][j] = grad_out[t] . y[r]          (fp32)
+ *   grad_y[r]  = top_k_weights[t][j] grad_out[t]           (r = dst_row[t*k+j])
+ *   grad_act   = grad_y W_d[e];  grad_g = grad_act u silu'(g),  grad_u = grad_act silu(g)
+ *   grad_x[r]  = grad_g W_g[e] + grad_u W_u[e]
+ *   grad_hidden_states[t] = sum_j grad_x[dst_row[t*k+j]]   (fp32 sum, rounded once)
+ *   grad_w_down[e]    = sum over e's rows of grad_y^T act    (fp32)
+ *   grad_w_gate_up[e] = sum over e's rows of [grad_g grad_u]^T x  (fp32)
+ * For MOE_BF16, g, u, act, y, grad_y, grad_g, grad_u and grad_x are bf16 in
+ * memory (each rounded once); products accumulate in fp32.
+ * --------------------------------------------------------------------------- */
+
+/* Bytes of workspace moe_chunked_backward needs (metadata plus min(N,2) slots of
+ * ceil(T/N)*k rows of 2H + 3I elements).  Host-only. */
+moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/*
+ * The whole backward.  Inputs as for moe_chunked_forward plus grad_out [T][H]
+ * (dtype of the layer).  Outputs, all overwritten:
+ *   grad_hidden_states [T][H] (layer dtype), grad_top_k_weights [T][k] fp32
+ *   (0 for dropped slots), grad_w_gate_up [E][2I][H] fp32, grad_w_down [E][H][I]
+ *   fp32 (zero for experts that receive no row).
+ * Dropped ids are counted into *dev_error (nullable).  Streams as for the
+ * forward: the memory-bound per-chunk steps of a pair run on s0 and s1, the
+ * GEMMs on s0; on return s0 is ordered after all work.  grad_hidden_states and
+ * grad_top_k_weights do not depend on N (same bits); the weight gradients sum
+ * the pairs' contributions in pair order, so they differ across N by rounding.
+ */
+moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_states,
+                                const int32_t* top_k_index, const float* top_k_weights,
+                                const void* w_gate_up, const void* w_down, const void* grad_out,
+                                void* grad_hidden_states, float* grad_top_k_weights,
+                                float* grad_w_gate_up, float* grad_w_down, int32_t* dev_error,
+                                void* ws, size_t ws_bytes, hipStream_t s0, hipStream_t s1);
+
+/*
+ * Combine backward of chunk `chunk`: for every assignment f = t*k + j of the
+ * chunk with r = dst_row[f] >= 0, grad_top_k_weights[f] = grad_out[t] . y[r]
+ * (fp32) and grad_y[r] = top_k_weights[f] * grad_out[t] (rounded once); dropped
+ * slots get grad_top_k_weights[f] = 0.  grad_out is the full [T][H] array, y and
+ * grad_y the chunk's [rows][H] buffers (grad_y may alias y).
+ */
+moe_status moe_unpermute_combine_backward(const moe_shape* shape, int32_t chunk,
+                                          const void* grad_out, const void* y,
+                                          const int32_t* dst_row, const float* top_k_weights,
+                                          void* grad_y, float* grad_top_k_weights,
+                                          hipStream_t stream);
+
+/*
+ * Permute backward of chunk `chunk`: grad_hidden[t] = sum over kept slots j of
+ * grad_x_perm[dst_row[t*k+j]], fp32 in ascending j, rounded once; rows [t0, t1)
+ * of grad_hidden only.
+ */
+moe_status moe_permute_backward(const moe_shape* shape, int32_t chunk, const void* grad_x_perm,
+                                const int32_t* dst_row, void* grad_hidden, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

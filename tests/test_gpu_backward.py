@@ -1,0 +1,248 @@
+"""Parity of the backward (moe_chunked_backward, through the C ABI) with the
+float64 CPU oracle's backward (oracle.moe_backward, itself pinned by finite
+differences of the forward).
+
+Tolerances (row-wise inf-norm relative error, rows of grad_hidden [T,H],
+grad_w [T,k], and of each expert's weight gradient):
+  fp32 workloads: 1e-5 -- fp32 accumulation only;
+  bf16 workloads: 3e-2 -- the bf16 path rounds g, u, act, y, grad_y,
+    grad_g/grad_u and grad_x once each (<= 2^-9 relative apiece); along the
+    longest chain (grad_x <- grad_g <- g, u, grad_act <- grad_y) four such
+    roundings compound to ~4 * 2^-9 ~ 0.8% per element before accumulation, so
+    the forward's 2e-2 bar is widened to 3e-2.
+grad_w[t,j] is a dot product over H whose terms cancel, and a row of an
+expert's weight gradient that only a few tokens reach is a scalar (itself such
+a dot product) times one input row, so those errors are measured against the
+whole array's scale: max |gpu - oracle| / max |oracle| over grad_w, and over
+each expert's grad_w_gate_up and grad_w_down (inf-norm relative error), with the
+same tolerances.
+grad_hidden and grad_w do not depend on the chunk count: compared bit for bit
+across N and stream settings.  Weight gradients sum per-pair partials in pair
+order, so across N they are compared with a 1e-5 relative bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_top_route_expert_amd as moe
+import oracle
+import synth
+from gpu_layer import build_layer, f64, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 3e-2}
+C = synth.CONFIGS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+
+
+_layers = {}
+
+
+def layer_for(name, T=None, idx=None, w=None):
+    key = (name, T, None if idx is None else idx.tobytes())
+    if key not in _layers:
+        if len(_layers) > 2:
+            _layers.clear()
+        cfg = C[name] if T is None else C[name].with_tokens(T)
+        _layers[key] = build_layer(cfg, idx, w)
+    return _layers[key]
+
+
+def norm_rel_err(got, ref):
+    """max |got - ref| / max |ref| over the whole array."""
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(np.asarray(got, np.float64) - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def grad_out_for(L, seed=11):
+    """Seeded upstream gradient of the layer's shape and dtype (N(0,1))."""
+    cfg = L.cfg
+    key = synth.stream_key(cfg.seed + 1000 * seed, 9, 0)
+    g = synth.normal(key, cfg.T * cfg.H, 1.0, "cuda").view(cfg.T, cfg.H)
+    return g.to(cfg.torch_dtype).contiguous()
+
+
+def run_backward(L, N, go, two_streams=True):
+    cfg = L.cfg
+    shape = L.shape(N)
+    dt = cfg.torch_dtype
+    gh = torch.full((cfg.T, cfg.H), float("nan"), dtype=dt, device="cuda")
+    gw = torch.full((cfg.T, cfg.k), float("nan"), dtype=torch.float32, device="cuda")
+    gwgu = torch.full((cfg.E, 2 * cfg.I, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+    gwd = torch.full((cfg.E, cfg.H, cfg.I), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_backward_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    err = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream() if two_streams else None
+    say(f"backward {cfg.name} T={cfg.T} N={N} two_streams={two_streams}")
+    moe.moe_chunked_backward(shape, L.hidden, L.idx, L.w, L.wgu, L.wd, go, gh, gw, gwgu, gwd, ws,
+                             err, s0=s0, s1=s1)
+    torch.cuda.synchronize()
+    return gh, gw, gwgu, gwd, int(err.item())
+
+
+def check_weight_grads(L, ref, gwgu, gwd, tol, experts=None):
+    cfg = L.cfg
+    experts = range(cfg.E) if experts is None else experts
+    for e in experts:
+        if e in ref["grad_wgu"]:
+            eg = norm_rel_err(f64(gwgu[e]), ref["grad_wgu"][e])
+            ed = norm_rel_err(f64(gwd[e]), ref["grad_wd"][e])
+            assert eg <= tol and ed <= tol, (e, eg, ed)
+        else:
+            assert bool((gwgu[e] == 0).all()) and bool((gwd[e] == 0).all()), e
+
+
+FULL = [("tiny_f32", 1, None), ("tiny_f32", 3, None), ("t3_n4", 4, None),
+        ("bf16_e64_zipf", 2, 256)]
+
+
+@pytest.mark.parametrize("name,N,T", FULL)
+def test_backward_every_output_vs_oracle(name, N, T):
+    L = layer_for(name, T)
+    cfg = L.cfg
+    go = grad_out_for(L)
+    gh, gw, gwgu, gwd, err = run_backward(L, N, go)
+    ref = oracle.moe_backward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I, f64(go),
+                              cfg.groups, N)
+    tol = TOL[cfg.dtype]
+    assert err == ref["meta"]["n_invalid"]
+    e_h = oracle.row_rel_err(f64(gh), ref["grad_hidden"])
+    e_w = norm_rel_err(f64(gw), ref["grad_w"])
+    say(f"  grad_hidden {e_h:.2e}  grad_w {e_w:.2e}")
+    assert e_h <= tol and e_w <= tol, (e_h, e_w)
+    check_weight_grads(L, ref, gwgu, gwd, tol)
+
+
+SAMPLED = [("bf16_e64_zipf", 2, 8, 4), ("dsv3_e256", 1, 4, 2), ("skew_two_experts", 1, 6, 2),
+           ("packed16k_e128", 4, 8, 3), ("decode_t64", 1, 6, 3)]
+
+
+@pytest.mark.parametrize("name,N,n_tok,n_exp", SAMPLED)
+def test_backward_sampled_vs_oracle(name, N, n_tok, n_exp):
+    L = layer_for(name)
+    cfg = L.cfg
+    go = grad_out_for(L)
+    gh, gw, gwgu, gwd, err = run_backward(L, N, go)
+    assert err == 0
+    rng = np.random.default_rng(3)
+    toks = sorted({0, cfg.T - 1, *[int(t) for t in rng.integers(0, cfg.T, n_tok)]})
+    ref_h, ref_w = oracle.moe_tokens_backward(toks, L.hidden64(), L.idx_np, L.w_np, L.expert64,
+                                              cfg.E, cfg.I, f64(go))
+    tol = TOL[cfg.dtype]
+    e_h = oracle.row_rel_err(f64(gh[toks]), ref_h)
+    e_w = norm_rel_err(f64(gw[toks]), ref_w)
+    say(f"  sampled grad_hidden {e_h:.2e}  grad_w {e_w:.2e}")
+    assert e_h <= tol and e_w <= tol, (e_h, e_w)
+    counts = np.bincount(L.idx_np[(L.idx_np >= 0) & (L.idx_np < cfg.E)], minlength=cfg.E)
+    active = [e for e in range(cfg.E) if counts[e] > 0]
+    by = sorted(active, key=lambda e: counts[e])
+    pick = sorted({by[0], by[-1], *[by[i] for i in np.linspace(0, len(by) - 1, n_exp).astype(int)]})
+    hid = L.hidden64()
+    for e in pick:
+        gwgu_ref, gwd_ref = oracle.expert_weight_grads(e, hid, L.idx_np, L.w_np, L.expert64, cfg.I,
+                                                       f64(go))
+        eg = norm_rel_err(f64(gwgu[e]), gwgu_ref)
+        ed = norm_rel_err(f64(gwd[e]), gwd_ref)
+        say(f"  expert {e} rows {counts[e]}: grad_w_gate_up {eg:.2e} grad_w_down {ed:.2e}")
+        assert eg <= tol and ed <= tol, (e, eg, ed)
+    for e in range(cfg.E):
+        if counts[e] == 0:
+            assert bool((gwgu[e] == 0).all()) and bool((gwd[e] == 0).all()), e
+
+
+@pytest.mark.parametrize("name,Ns", [("bf16_e64_zipf", (2, 4)), ("tiny_f32", (2, 5)),
+                                     ("packed16k_e128", (2, 8)), ("t3_n4", (4,))])
+def test_backward_chunk_invariance(name, Ns):
+    L = layer_for(name)
+    go = grad_out_for(L)
+    base = run_backward(L, 1, go, two_streams=False)
+    for N in Ns:
+        for two in (True, False):
+            gh, gw, gwgu, gwd, _ = run_backward(L, N, go, two_streams=two)
+            assert torch.equal(gh, base[0]), (N, two)
+            assert torch.equal(gw, base[1]), (N, two)
+            for got, want in ((gwgu, base[2]), (gwd, base[3])):
+                den = want.abs().flatten(1).amax(dim=1).clamp_min(1e-30)
+                rel = ((got - want).abs().flatten(1).amax(dim=1) / den).max().item()
+                assert rel <= 1e-5, (N, two, rel)
+
+
+def test_backward_steps_vs_oracle_pieces():
+    """moe_unpermute_combine_backward and moe_permute_backward on their own."""
+    L = layer_for("bf16_e64_zipf", 512)
+    cfg = L.cfg
+    shape = L.shape(2)
+    go = grad_out_for(L)
+    meta = oracle.route_meta(L.idx_np, cfg.E, 1, 2)
+    dst = torch.from_numpy(meta["dst_row"].astype(np.int32)).cuda()
+    t0, t1 = moe.moe_chunk_range(shape, 1)
+    rows = (t1 - t0) * cfg.k
+    valid = int(meta["offsets"][1][cfg.E])
+    key = synth.stream_key(77, 9, 1)
+    y = synth.normal(key, rows * cfg.H, 1.0, "cuda").view(rows, cfg.H).to(cfg.torch_dtype)
+    gy = torch.full_like(y, 555.0)
+    gw = torch.full((cfg.T, cfg.k), -3.0, dtype=torch.float32, device="cuda")
+    say("combine backward step")
+    moe.moe_unpermute_combine_backward(shape, 1, go, y, dst, L.w, gy, gw)
+    torch.cuda.synchronize()
+    d = meta["dst_row"][t0 * cfg.k:t1 * cfg.k].reshape(-1, cfg.k)
+    y64, go64, w64 = f64(y), f64(go), L.w_np.astype(np.float64)
+    want_w = np.zeros((t1 - t0, cfg.k))
+    for t in range(t1 - t0):
+        for j in range(cfg.k):
+            r = d[t, j]
+            if r >= 0:
+                want_w[t, j] = go64[t0 + t] @ y64[r]
+                rel = np.abs(f64(gy[r]) - w64[t0 + t, j] * go64[t0 + t]).max() / \
+                    max(np.abs(w64[t0 + t, j] * go64[t0 + t]).max(), 1e-30)
+                assert rel <= 2 ** -8, (t, j, rel)
+    assert norm_rel_err(f64(gw[t0:t1]), want_w) <= 1e-5
+    assert bool((gw[:t0] == -3.0).all())
+    assert bool((gy[valid:] == 555.0).all())
+    # permute backward: grad_hidden[t] = sum_j g[dst_row[t*k+j]]
+    gh = torch.full((cfg.T, cfg.H), 777.0, dtype=cfg.torch_dtype, device="cuda")
+    say("permute backward step")
+    moe.moe_permute_backward(shape, 1, y, dst, gh)
+    torch.cuda.synchronize()
+    want = np.zeros((t1 - t0, cfg.H))
+    for j in range(cfg.k):
+        keep = d[:, j] >= 0
+        want[keep] += y64[d[keep, j]]
+    assert oracle.row_rel_err(f64(gh[t0:t1]), want) <= 2 ** -8
+    assert bool((gh[:t0] == 777.0).all())
+
+
+def test_backward_dropped_ids_and_zero_tokens():
+    cfg = C["tiny_f32"]
+    idx, w = synth.routing(cfg)
+    idx = idx.copy()
+    idx[5, :] = -1
+    idx[9, 1] = cfg.E
+    L = build_layer(cfg, idx, w)
+    go = grad_out_for(L)
+    for N in (1, 3):
+        gh, gw, gwgu, gwd, err = run_backward(L, N, go)
+        ref = oracle.moe_backward(L.hidden64(), idx, w, L.expert64, cfg.E, cfg.I, f64(go), 1, N)
+        assert err == ref["meta"]["n_invalid"] == cfg.k + 1
+        assert oracle.row_rel_err(f64(gh), ref["grad_hidden"]) <= TOL["f32"]
+        assert bool((gh[5] == 0).all()) and bool((gw[5] == 0).all()) and float(gw[9, 1]) == 0.0
+        check_weight_grads(L, ref, gwgu, gwd, TOL["f32"])
+    # no tokens: the weight gradients are zero
+    z = moe.make_shape(0, cfg.H, cfg.E, cfg.k, cfg.I, 1, 2, "f32")
+    gwgu = torch.full((cfg.E, 2 * cfg.I, cfg.H), 5.0, device="cuda")
+    gwd = torch.full((cfg.E, cfg.H, cfg.I), 5.0, device="cuda")
+    ws = torch.empty(moe.moe_backward_workspace_size(z), dtype=torch.uint8, device="cuda")
+    e0 = torch.empty(0, device="cuda")
+    say("backward zero tokens")
+    moe.moe_chunked_backward(z, e0, torch.empty(0, dtype=torch.int32, device="cuda"), e0, L.wgu,
+                             L.wd, e0, e0, e0, gwgu, gwd, ws)
+    torch.cuda.synchronize()
+    assert bool((gwgu == 0).all()) and bool((gwd == 0).all())

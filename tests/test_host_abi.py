@@ -76,6 +76,16 @@ def test_workspace_follows_pair_model():
     for n, f in frac.items():
         assert sizes[int(n)] / sizes[1] == f
     assert sizes[8] / sizes[1] == 0.25
+    # backward: the same pair residency, slots of (2H + 3I) elements per row
+    bsizes = {}
+    for N in (1, 2, 4, 8):
+        shape = moe.make_shape(T, H, E, k, I, 1, N, "bf16")
+        ws = moe.moe_backward_workspace_size(shape)
+        slots = oracle.w_pair_rows(T, N, k) * (2 * H + 3 * I) * 2
+        assert 0 < ws - slots < 8 * T * k + 16 * 1024 * 1024, (N, ws - slots)
+        bsizes[N] = slots
+    for n, f in frac.items():
+        assert bsizes[int(n)] / bsizes[1] == f
 
 
 def test_route_meta_workspace_positive():
@@ -147,6 +157,21 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                 fake, None) == 1
     assert _raw("moe_expert_ffn_pair", sp, 2, fake, fake, fake, fake, fake, fake, fake, fake,
                 None) == 1
+    # backward: too-small workspace, misaligned grad_out, null weight gradients
+    need_b = moe.moe_backward_workspace_size(shape)
+    args = [fake] * 10  # hidden .. grad_w_down
+    assert _raw("moe_chunked_backward", sp, *args, None, fake, need_b - 1, None, None) == 3
+    bad = list(args)
+    bad[5] = fake + 2
+    assert _raw("moe_chunked_backward", sp, *bad, None, fake, need_b, None, None) == 1
+    bad = list(args)
+    bad[8] = None
+    assert _raw("moe_chunked_backward", sp, *bad, None, fake, need_b, None, None) == 1
+    assert _raw("moe_unpermute_combine_backward", sp, 2, fake, fake, fake, fake, fake, fake,
+                None) == 1
+    assert _raw("moe_unpermute_combine_backward", sp, 0, fake, fake, fake, fake, None, fake,
+                None) == 1
+    assert _raw("moe_permute_backward", sp, 0, fake + 4, fake, fake, None) == 1
     # unknown schedule
     for sched in (-1, 2):
         assert _raw("moe_chunked_forward_schedule", sp, fake, fake, fake, fake, fake, fake, None,
@@ -161,6 +186,9 @@ def test_empty_chunk_calls_are_noops():
     assert _raw("moe_permute", sp, 3, None, None, None, None) == 0
     assert _raw("moe_expert_ffn", sp, 3, None, None, None, None, None, None, None) == 0
     assert _raw("moe_unpermute_combine", sp, 3, None, None, None, None, None) == 0
+    assert _raw("moe_unpermute_combine_backward", sp, 3, None, None, None, None, None, None,
+                None) == 0
+    assert _raw("moe_permute_backward", sp, 3, None, None, None, None) == 0
     # a pair whose chunks are both empty; none of its pointers is needed
     assert _raw("moe_expert_ffn_pair", sp, 3, None, None, None, None, None, None, None, None,
                 None) == 0
