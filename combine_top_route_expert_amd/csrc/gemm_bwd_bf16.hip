@@ -21,9 +21,10 @@
 // of LDS row k sits at slot c ^ 4(k mod 4), which spreads the 4 rows x 4 chunks
 // a 32-lane phase reads over 16 distinct bank groups.
 //
-// Grouping and XCD placement follow the forward kernels (MTileMap, xcd_tile);
-// the wgrad tiles are numbered (expert, m-tile) and its K loop runs over the
-// expert's rows of both chunks; rows past the expert's block are loaded from a
+// The dgrad groups and places tiles like the forward kernels (MTileMap,
+// xcd_tile); the wgrad tiles are numbered (expert, m-tile), dealt to the XCDs
+// round-robin (xcd_tile_rr), and the K loop runs over the expert's rows of both
+// chunks; rows past the expert's block are loaded from a
 // clamped row and zeroed in the A fragment.
 #include "moe_internal.h"
 
@@ -41,6 +42,12 @@ constexpr int BK = 64;
 constexpr int wait_vm(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
+// Forces v to be computed at this point (an empty asm that reads it), so the
+// compiler cannot sink the arithmetic below later stores; the waits for the
+// loads it consumes then come before the first store, not after each one.
+__device__ __forceinline__ void pin(uint32_t v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
@@ -55,6 +62,46 @@ struct Side {
   int split;
   int64_t ld;  // elements per row
 };
+
+// The two base addresses as wave-uniform integers.  Selecting between them per
+// lane as integers keeps the compiler from turning the choice into a per-lane
+// load of the pointer from the argument block (whose wait would also drain the
+// loads in flight).
+struct SideU {
+  uint64_t b0, b1;
+  int split;
+  int64_t ld;
+};
+
+__device__ __forceinline__ uint64_t uniform_u64(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ SideU uniform_side(const Side& s) {
+  SideU u;
+  u.b0 = uniform_u64(s.p[0]);
+  u.b1 = uniform_u64(s.p[1]);
+  u.split = s.split;
+  u.ld = s.ld;
+  return u;
+}
+
+// Byte address of element `col` of virtual row v of the tile's expert.
+__device__ __forceinline__ uint64_t side_addr(const SideU& s, const TileRows& tr, int v, int col) {
+  int64_t row;
+  uint64_t shift = 0;  // b1 - b0 for rows of the second chunk (added, not selected)
+  if (s.split) {
+    const bool second = v >= tr.n0;
+    row = second ? tr.lo1 + (v - tr.n0) : tr.lo0 + v;
+    shift = second ? s.b1 - s.b0 : 0ull;
+  } else {
+    row = (int64_t)tr.joint_row(v);
+  }
+  return s.b0 + shift + (uint64_t)(row * s.ld + col) * 2u;
+}
 
 __device__ __forceinline__ const uint16_t* side_row(const Side& s, const TileRows& tr, int v) {
   if (s.split) {
@@ -212,6 +259,59 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
 
   // epilogue: lane l holds column l % 32 of rows 8(q/4) + 4(l/32) + q%4 of each block
   const int rbase = wm * WM + 4 * (lane >> 5);
+  if constexpr (kEpi == kDgradSwiglu) {
+    // per 8-row half block: all of its g/u loads first, then the arithmetic and
+    // the stores, so one wait covers the half block (a wait per row would also
+    // wait for every earlier store)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // rows q = 8h .. 8h+7 of the block
+        uint16_t gv[8][FN], uv[8][FN];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int q = 8 * h + qq;
+          const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+          const int rr = row < tr.rows ? row : tr.rows - 1;
+          const uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + rr) * (2 * a.I);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            int col = nt * BN + wn * WN + j * 32 + (lane & 31);
+            col = col < a.N ? col : a.N - 1;
+            gv[qq][j] = gr[col];
+            uv[qq][j] = gr[a.I + col];
+          }
+        }
+        // all arithmetic before any store: no loaded value is used after a store
+        uint32_t gu_out[8][FN];  // grad_u << 16 | grad_g
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const float ga = acc[i][j][8 * h + qq];
+            const float g = bf16_to_f32(gv[qq][j]), u = bf16_to_f32(uv[qq][j]);
+            const float sg = 1.0f / (1.0f + expf(-g));
+            gu_out[qq][j] = (uint32_t)to_bf16_bits(ga * u * (sg + g * sg * (1.0f - sg))) |
+                            ((uint32_t)to_bf16_bits(ga * (g * sg)) << 16);
+            pin(gu_out[qq][j]);
+          }
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+          const int q = 8 * h + qq;
+          const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+          if (row >= tr.rows) continue;
+          uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
+            if (col >= a.N) continue;
+            gr[col] = (uint16_t)(gu_out[qq][j] & 0xffffu);
+            gr[a.I + col] = (uint16_t)(gu_out[qq][j] >> 16);
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -219,19 +319,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
       const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
       if (row >= tr.rows) continue;
       const int v = tr.v0 + row;
-      if constexpr (kEpi == kDgradSwiglu) {
-        uint16_t* gr = a.gu + (int64_t)tr.joint_row(v) * (2 * a.I);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
-          if (col >= a.N) continue;
-          const float ga = acc[i][j][q];
-          const float g = bf16_to_f32(gr[col]), u = bf16_to_f32(gr[a.I + col]);
-          const float s = 1.0f / (1.0f + expf(-g));
-          gr[col] = to_bf16_bits(ga * u * (s + g * s * (1.0f - s)));
-          gr[a.I + col] = to_bf16_bits(ga * (g * s));
-        }
-      } else {
+      {
         uint16_t* cr;
         if (a.c_split) {
           int part;
@@ -277,7 +365,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   int emt, nt;
-  if (!xcd_tile(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
+  if (!xcd_tile_rr(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
   const int e = emt / a.m_tiles, mt = emt - e * a.m_tiles;
   TileRows tr;
   tr.e = e;
@@ -304,20 +392,21 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
     int col = nt * BN + 8 * ((lane % GB::SLOTS) ^ GB::swz(b_k[t]));
     b_col[t] = col > a.N - 8 ? a.N - 8 : col;
   }
+  const SideU sa_u = uniform_side(a.a), sb_u = uniform_side(a.b);
   auto issue = [&](int kt, int buf) {
     char* base = smem + buf * STAGE;
 #pragma unroll
     for (int t = 0; t < LA; ++t) {
       int v = kt * BK + a_k[t];
       v = v < rows ? v : rows - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(side_row(a.a, tr, v) + a_col[t]),
+      __builtin_amdgcn_global_load_lds((const void*)side_addr(sa_u, tr, v, a_col[t]),
                                        (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < LB; ++t) {
       int v = kt * BK + b_k[t];
       v = v < rows ? v : rows - 1;
-      __builtin_amdgcn_global_load_lds((const void*)(side_row(a.b, tr, v) + b_col[t]),
+      __builtin_amdgcn_global_load_lds((const void*)side_addr(sb_u, tr, v, b_col[t]),
                                        (lds_void*)(base + GA::STAGE_BYTES + (wave * LB + t) * 1024),
                                        16, 0, 0);
     }
@@ -372,6 +461,42 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
 
   float* Ce = a.C + (int64_t)e * a.M * a.N;
   const int rbase = wm * WM + 4 * (lane >> 5);
+  if (a.accumulate) {
+    // per 32-row block: all loads of the previous sums first, then the stores
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float old[16][FN];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        int m = mt * BM + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        m = m < a.M ? m : a.M - 1;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          int n = nt * BN + wn * WN + j * 32 + (lane & 31);
+          n = n < a.N ? n : a.N - 1;
+          old[q][j] = Ce[(int64_t)m * a.N + n];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          old[q][j] += acc[i][j][q];
+          pin(old[q][j]);
+        }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int m = mt * BM + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = nt * BN + wn * WN + j * 32 + (lane & 31);
+          if (n < a.N) Ce[(int64_t)m * a.N + n] = old[q][j];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -382,8 +507,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int n = nt * BN + wn * WN + j * 32 + (lane & 31);
-        if (n >= a.N) continue;
-        cr[n] = a.accumulate ? cr[n] + acc[i][j][q] : acc[i][j][q];
+        if (n < a.N) cr[n] = acc[i][j][q];
       }
     }
 }

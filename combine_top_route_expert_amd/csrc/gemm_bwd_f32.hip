@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(kThreads) wgrad_gemm_f32(WgradArgsF a) {
   __shared__ float Bs[BKF][BN];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   int emt, nt;
-  if (!xcd_tile(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
+  if (!xcd_tile_rr(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
   const int e = emt / a.m_tiles, mt = emt - e * a.m_tiles;
   TileRows tr;
   tr.e = e;

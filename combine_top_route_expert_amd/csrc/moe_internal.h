@@ -224,6 +224,19 @@ __device__ __forceinline__ bool xcd_tile(int total, int n_tiles, int* mt, int* n
   return *mt < total;
 }
 
+// Round-robin variant: XCD x takes m-tiles x, x + 8, x + 16, ... (each with all
+// its n-tiles).  For the weight-gradient products, whose m-tiles are (expert,
+// row block) pairs with a reduction as long as the expert's row count, this
+// spreads each heavily loaded expert over all eight XCDs instead of queueing
+// it on one.  Same grid as xcd_tile.
+__device__ __forceinline__ bool xcd_tile_rr(int total, int n_tiles, int* mt, int* nt) {
+  const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int ml = q / n_tiles;
+  *mt = ml * 8 + x;
+  *nt = q - ml * n_tiles;
+  return *mt < total;
+}
+
 // Host side: grid of xcd_tile for a bound on the m-tiles.
 inline int64_t xcd_grid(int64_t m_tiles_bound, int n_tiles) {
   return 8 * ((m_tiles_bound + 7) / 8) * (int64_t)n_tiles;
