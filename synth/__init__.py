@@ -219,6 +219,12 @@ CONFIGS = {
     # every slot routed to expert 0 or 1 (maximal skew)
     "skew_two_experts": MoEConfig("skew_two_experts", 7, 3, 1000, 7168, 256, 8, 2048, "bf16",
                                   "two_experts", None, 16, (1,)),
+    # sizes off the tile grids: H = 5*64, I = 3*64 (partial column tiles everywhere)
+    "odd_dims_bf16": MoEConfig("odd_dims_bf16", 8, 8, 1536, 320, 8, 4, 192, "bf16", "normal",
+                               0.5, 2, (1, 3)),
+    # fp32 sizes that are multiples of 4 only, with a ragged token count
+    "odd_dims_f32": MoEConfig("odd_dims_f32", 9, 9, 203, 36, 5, 3, 20, "f32", "normal", None, 1,
+                              (1, 4)),
 }
 
 

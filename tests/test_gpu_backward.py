@@ -101,7 +101,8 @@ def check_weight_grads(L, ref, gwgu, gwd, tol, experts=None):
 
 
 FULL = [("tiny_f32", 1, None), ("tiny_f32", 3, None), ("t3_n4", 4, None),
-        ("bf16_e64_zipf", 2, 256)]
+        ("bf16_e64_zipf", 2, 256), ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None),
+        ("odd_dims_f32", 4, None)]
 
 
 @pytest.mark.parametrize("name,N,T", FULL)
@@ -159,7 +160,8 @@ def test_backward_sampled_vs_oracle(name, N, n_tok, n_exp):
 
 
 @pytest.mark.parametrize("name,Ns", [("bf16_e64_zipf", (2, 4)), ("tiny_f32", (2, 5)),
-                                     ("packed16k_e128", (2, 8)), ("t3_n4", (4,))])
+                                     ("packed16k_e128", (2, 8)), ("t3_n4", (4,)),
+                                     ("odd_dims_bf16", (3,)), ("odd_dims_f32", (4,))])
 def test_backward_chunk_invariance(name, Ns):
     L = layer_for(name)
     go = grad_out_for(L)

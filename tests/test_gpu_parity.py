@@ -197,7 +197,8 @@ def test_expert_ffn_vs_oracle(name, N, n_experts):
 
 # --------------------------------------------------------------------- whole layer
 FULL_CASES = [("tiny_f32", 1, None), ("t3_n4", 4, None), ("t3_n4", 1, None),
-              ("bf16_e64_zipf", 1, 1024), ("bf16_e64_zipf", 2, 1000)]
+              ("bf16_e64_zipf", 1, 1024), ("bf16_e64_zipf", 2, 1000),
+              ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None), ("odd_dims_f32", 4, None)]
 
 
 @pytest.mark.parametrize("name,N,T", FULL_CASES)
@@ -231,7 +232,8 @@ def test_forward_sampled_tokens_vs_oracle(name, N, n_tok):
 
 @pytest.mark.parametrize("name,Ns", [("bf16_e64_zipf", (2,)), ("packed16k_e128", (2, 4, 8)),
                                      ("t3_n4", (4,)), ("dsv3_e256", (3,)),
-                                     ("tiny_f32", (2, 5))])
+                                     ("tiny_f32", (2, 5)), ("odd_dims_bf16", (3,)),
+                                     ("odd_dims_f32", (4,))])
 def test_chunked_equals_unchunked_bitwise(name, Ns):
     L = layer_for(name)
     base, _ = run_forward(L, L.shape(1), two_streams=False)
