@@ -539,29 +539,25 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
                                     err, w + p.meta_ws, s0);
   if (he != hipSuccess) return MOE_ERR_HIP;
 
-  const bool two = (s1 != nullptr && s1 != s0 && s.N >= 2);
-  hipEvent_t ev[kEvents] = {};
-  if (two) {
-    he = thread_events(ev);
-    if (he == hipSuccess) he = join(s1, s0, ev[0]);
-    if (he != hipSuccess) return MOE_ERR_HIP;
-  }
-  bool used_s1 = false, first = true;
+  // Every step runs on s0: as in the pair-fused forward, the joins that
+  // would let a pair's second permute / combine backward / permute backward
+  // run on s1 cost more than that overlap gains.  s1 is accepted for the
+  // interface's sake.
+  (void)s1;
+  bool first = true;
   auto chunk_rows = [&](int c, int* t0, int* t1) {
     *t0 = *t1 = 0;
     if (c < s.N) chunk_tokens(s, c, t0, t1);
     return (int64_t)(*t1 - *t0) * s.k;
   };
-  // Pair (c, c+1): permutes (c on s0, c+1 on s1); on s0: gate_up (act and the
-  // saved g/u), down (y), then after the combine backwards (c on s0, c+1 on s1):
-  // dgrad of down with the SwiGLU backward (grad_g/grad_u over g/u), the W_d
-  // wgrad, the gate/up dgrad (grad_x over y's buffer), the W_gu wgrad; then the
-  // permute backwards (c on s0, c+1 on s1).
+  // Pair (c, c+1): both permutes, gate_up (act and the saved g/u), down (y),
+  // both combine backwards, the dgrad of down with the SwiGLU backward
+  // (grad_g/grad_u over g/u), the W_d wgrad, the gate/up dgrad (grad_x over y's
+  // buffer), the W_gu wgrad, then both permute backwards.
   for (int c = 0; c < s.N; c += 2) {
     int t0, t1, u0, u1;
     const int64_t rows0 = chunk_rows(c, &t0, &t1), rows1 = chunk_rows(c + 1, &u0, &u1);
     if (rows0 + rows1 == 0) continue;
-    hipStream_t st1 = two ? s1 : s0;
     void* xp0 = w + p.xp[0];
     void* xp1 = p.nslots > 1 ? w + p.xp[1] : nullptr;
     void* yg0 = w + p.yg[0];
@@ -569,11 +565,7 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     const int32_t* off0 = offsets + (size_t)c * (s.E + 1);
     const int32_t* off1 = rows1 > 0 ? off0 + (s.E + 1) : nullptr;
     he = launch_permute(s, t0, t1, hidden_states, dst_row, xp0, s0);
-    if (he == hipSuccess && rows1 > 0) he = launch_permute(s, u0, u1, hidden_states, dst_row, xp1, st1);
-    if (he == hipSuccess && two && rows1 > 0) {
-      used_s1 = true;
-      he = join(s0, s1, ev[1]);
-    }
+    if (he == hipSuccess && rows1 > 0) he = launch_permute(s, u0, u1, hidden_states, dst_row, xp1, s0);
     if (he != hipSuccess) return MOE_ERR_HIP;
     // forward recompute: act + saved g/u, then y
     GroupedIO io{};
@@ -596,17 +588,12 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     io.c_split = true;
     st = down(s, io, w_down, s0);
     if (st != MOE_OK) return st;
-    if (two && rows1 > 0) {
-      he = join(s1, s0, ev[2]);
-      if (he != hipSuccess) return MOE_ERR_HIP;
-    }
     // combine backward: grad_w rows of the pair's tokens, grad_y over y
     he = launch_combine_backward(s, t0, t1, grad_out, yg0, dst_row, top_k_weights, yg0,
                                  grad_top_k_weights, s0);
     if (he == hipSuccess && rows1 > 0)
       he = launch_combine_backward(s, u0, u1, grad_out, yg1, dst_row, top_k_weights, yg1,
-                                   grad_top_k_weights, st1);
-    if (he == hipSuccess && two && rows1 > 0) he = join(s0, s1, ev[1]);
+                                   grad_top_k_weights, s0);
     if (he != hipSuccess) return MOE_ERR_HIP;
     // dgrad of down with the SwiGLU backward: g/u -> grad_g/grad_u
     DgradIO dd{};
@@ -667,14 +654,10 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     st = wgrad(s, wg, s0);
     if (st != MOE_OK) return st;
     first = false;
-    if (two && rows1 > 0) {
-      he = join(s1, s0, ev[2]);
-      if (he != hipSuccess) return MOE_ERR_HIP;
-    }
     // permute backward: grad_hidden[t] = sum_j grad_x[dst_row[t*k+j]]
     he = launch_combine(s, t0, t1, yg0, dst_row, nullptr, grad_hidden, s0);
     if (he == hipSuccess && rows1 > 0)
-      he = launch_combine(s, u0, u1, yg1, dst_row, nullptr, grad_hidden, st1);
+      he = launch_combine(s, u0, u1, yg1, dst_row, nullptr, grad_hidden, s0);
     if (he != hipSuccess) return MOE_ERR_HIP;
   }
   if (first) {
@@ -694,10 +677,6 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     z.N = s.H;
     st = wgrad(s, z, s0);
     if (st != MOE_OK) return st;
-  }
-  if (two && used_s1) {
-    he = join(s0, s1, ev[1]);
-    if (he != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
 }
@@ -737,7 +716,9 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
   if (he != hipSuccess) return MOE_ERR_HIP;
   if (s.T == 0) return MOE_OK;
 
-  const bool two = (s1 != nullptr && s1 != s0 && s.N >= 2);
+  // only the per-chunk schedule uses s1
+  const bool two = (s1 != nullptr && s1 != s0 && s.N >= 2 &&
+                    schedule == MOE_SCHEDULE_PER_CHUNK);
   hipEvent_t ev[kEvents] = {};
   if (two) {
     he = thread_events(ev);
@@ -752,33 +733,27 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
   };
 
   if (schedule == MOE_SCHEDULE_PAIR_FUSED) {
-    // Pair (c, c+1): both permutes (c on s0, c+1 on s1), then one gate_up and
-    // one down launch over the pair's rows on s0, then both combines (c on s0,
-    // c+1 on s1).  Every expert's weights are streamed once per pair.
+    // Pair (c, c+1): both permutes, one gate_up and one down launch over the
+    // pair's rows, both combines, all on s0.  Every expert's weights are
+    // streamed once per pair.  (Running the second chunk's permute and combine
+    // on s1 measured slower: the stream joins cost more than overlapping two
+    // memory-bound kernels gains.)
     for (int c = 0; c < s.N; c += 2) {
       int t0, t1, u0, u1;
       const int64_t rows0 = chunk_rows(c, &t0, &t1), rows1 = chunk_rows(c + 1, &u0, &u1);
       if (rows0 + rows1 == 0) continue;  // empty tail pair
-      hipStream_t st1 = two ? s1 : s0;
+      hipStream_t st1 = s0;
       void* xy0 = w + p.slot[0];
       void* xy1 = p.nslots > 1 ? w + p.slot[1] : nullptr;
       he = launch_permute(s, t0, t1, hidden_states, dst_row, xy0, s0);
       if (he == hipSuccess && rows1 > 0)
         he = launch_permute(s, u0, u1, hidden_states, dst_row, xy1, st1);
-      if (he == hipSuccess && two && rows1 > 0) {
-        used_s1 = true;
-        he = join(s0, s1, ev[1]);
-      }
       if (he != hipSuccess) return MOE_ERR_HIP;
       const int32_t* off0 = offsets + (size_t)c * (s.E + 1);
       // y overwrites the dead x_perm of each slot
       st = pair_ffn(s, off0, off0 + (s.E + 1), rows0, rows1, xy0, xy1, w_gate_up, w_down,
                     w + p.slot_act[0], xy0, xy1, s0);
       if (st != MOE_OK) return st;
-      if (two && rows1 > 0) {
-        he = join(s1, s0, ev[2]);
-        if (he != hipSuccess) return MOE_ERR_HIP;
-      }
       he = launch_combine(s, t0, t1, xy0, dst_row, top_k_weights, out, s0);
       if (he == hipSuccess && rows1 > 0)
         he = launch_combine(s, u0, u1, xy1, dst_row, top_k_weights, out, st1);

@@ -230,9 +230,10 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  * Metadata for all chunks runs once on s0.  Adjacent chunks (0,1), (2,3), ...
  * form pairs; at most two chunks are resident (workspace slots 0 and 1), and a
  * last odd chunk runs alone.
- *  MOE_SCHEDULE_PAIR_FUSED: permute c on s0 while permute c+1 runs on s1; one
- *    gate_up and one down launch over the pair's rows on s0 (moe_expert_ffn_pair);
- *    combine c on s0 while combine c+1 runs on s1.
+ *  MOE_SCHEDULE_PAIR_FUSED: both permutes of the pair, one gate_up and one down
+ *    launch over the pair's rows (moe_expert_ffn_pair), both combines, all on
+ *    s0 (s1 is not used: on MI355X the joins that would let the second chunk's
+ *    permute and combine overlap on s1 cost more than the overlap gains).
  *  MOE_SCHEDULE_PER_CHUNK: chunk c runs permute -> gate_up -> down -> combine on
  *    stream s[c % 2] in slot c % 2, so the two chunks of a pair overlap as whole
  *    pipelines; every chunk streams the expert weights again.
@@ -283,9 +284,9 @@ moe_status moe_backward_workspace_size(const moe_shape* shape, size_t* bytes);
  *   grad_hidden_states [T][H] (layer dtype), grad_top_k_weights [T][k] fp32
  *   (0 for dropped slots), grad_w_gate_up [E][2I][H] fp32, grad_w_down [E][H][I]
  *   fp32 (zero for experts that receive no row).
- * Dropped ids are counted into *dev_error (nullable).  Streams as for the
- * forward: the memory-bound per-chunk steps of a pair run on s0 and s1, the
- * GEMMs on s0; on return s0 is ordered after all work.  grad_hidden_states and
+ * Dropped ids are counted into *dev_error (nullable).  As in the forward's
+ * pair-fused schedule every step runs on s0 (s1 may be null and is not used);
+ * on return s0 is ordered after all work.  grad_hidden_states and
  * grad_top_k_weights do not depend on N (same bits); the weight gradients sum
  * the pairs' contributions in pair order, so they differ across N by rounding.
  */
