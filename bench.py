@@ -116,6 +116,31 @@ def time_backward(moe, torch, shape, inp, steps, warmup):
     return ms, ws.numel()
 
 
+def time_graph(moe, torch, shape, inp, steps):
+    """The same layer step captured once in a HIP graph and replayed: removes the
+    host launch cost and the gaps between the step's kernels."""
+    out = torch.empty((shape.T, shape.H), dtype=shape.torch_dtype, device="cuda")
+    ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"], inp["wd"],
+                                out, ws, None, s0=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"], inp["wd"],
+                                out, ws, None, s0=torch.cuda.current_stream())
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def per_step_times(moe, torch, shape, inp, reps, flush_bytes=0):
     """Median and minimum of single-step times (HIP events around each step).  With
     flush_bytes > 0 a scratch buffer of that size is written before every step,
@@ -306,6 +331,8 @@ def main():
     log(f"layer N={N}, per-chunk schedule")
     run_pc = time_layer(moe, torch, shape, inp, args.steps, args.warmup,
                         schedule=moe.MOE_SCHEDULE_PER_CHUNK)
+    log("layer replayed from a HIP graph")
+    graph_ms = time_graph(moe, torch, shape, inp, args.steps)
     log("single steps, warm and with L2/MALL flushed")
     warm = per_step_times(moe, torch, shape, inp, 20)
     cold = per_step_times(moe, torch, shape, inp, 20, flush_bytes=1 << 30)
@@ -352,6 +379,8 @@ def main():
         "unchunked": {"ms_per_step": run1["wall_ms"], "value": cfg.T / (run1["wall_ms"] * 1e-3)},
         "per_chunk_schedule": {"ms_per_step": run_pc["wall_ms"],
                                "value": cfg.T / (run_pc["wall_ms"] * 1e-3)},
+        "hip_graph": {"ms_per_step": graph_ms, "value": cfg.T / (graph_ms * 1e-3),
+                      "note": "the same step captured once and replayed"},
         "single_step": {"warm": warm, "cold": cold},
         "backward": {"ms_per_step": bwd_ms, "value": cfg.T / (bwd_ms * 1e-3),
                      "flop_per_step": 18.0 * A_valid * H * I,

@@ -374,3 +374,51 @@ def test_zero_tokens():
                             torch.zeros(cfg.E * cfg.H * cfg.I, device="cuda"), z, ws, err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+
+
+def test_forward_and_backward_in_hip_graph():
+    """The pair-fused forward and the backward issue only kernels on s0 (no
+    events, memsets or host reads), so they can be captured in a HIP graph; every
+    replay, with eager work and synchronisations between replays, gives the
+    eager bits."""
+    L = layer_for("bf16_e64_zipf", 1024)
+    cfg = L.cfg
+    shape = L.shape(2)
+    eager, _ = run_forward(L, shape)
+    out = torch.zeros_like(eager)
+    ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    bshape = L.shape(2)
+    gh = torch.zeros((cfg.T, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+    gw = torch.zeros((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    gwgu = torch.zeros((cfg.E, 2 * cfg.I, cfg.H), dtype=torch.float32, device="cuda")
+    gwd = torch.zeros((cfg.E, cfg.H, cfg.I), dtype=torch.float32, device="cuda")
+    bws = torch.empty(moe.moe_backward_workspace_size(bshape), dtype=torch.uint8, device="cuda")
+    go = L.hidden  # any [T,H] tensor of the layer dtype
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        moe.moe_chunked_forward(shape, L.hidden, L.idx, L.w, L.wgu, L.wd, out, ws, s0=s)
+        moe.moe_chunked_backward(bshape, L.hidden, L.idx, L.w, L.wgu, L.wd, go, gh, gw, gwgu, gwd,
+                                 bws, s0=s)
+    torch.cuda.synchronize()
+    ref_b = [t.clone() for t in (gh, gw, gwgu, gwd)]
+    g = torch.cuda.CUDAGraph()
+    say("capture forward + backward")
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_chunked_forward(shape, L.hidden, L.idx, L.w, L.wgu, L.wd, out, ws,
+                                s0=torch.cuda.current_stream())
+        moe.moe_chunked_backward(bshape, L.hidden, L.idx, L.w, L.wgu, L.wd, go, gh, gw, gwgu, gwd,
+                                 bws, s0=torch.cuda.current_stream())
+    for rep in range(4):
+        out.fill_(float("nan"))
+        gh.fill_(float("nan"))
+        gwgu.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        for got, want in zip((gh, gw, gwgu, gwd), ref_b):
+            assert torch.equal(got, want), rep
+        # eager work between replays
+        run_forward(L, shape)
