@@ -2,10 +2,11 @@
 """MoE-layer benchmark on one MI355X.
 
 A step is one moe_chunked_forward call: routing metadata for every chunk,
-then per chunk pair: the two permutes on two HIP streams, one gate/up GEMM +
-SwiGLU launch and one down GEMM launch over both chunks' rows, the two
-weighted combines on two streams.  The per-chunk schedule (every chunk runs
-all four steps on its own stream) is timed beside it.  Inputs are seeded
+then per chunk pair, on one HIP stream: one gate/up GEMM + SwiGLU launch over
+both chunks' rows that gathers its rows straight from hidden_states (the
+permute fused into its row addressing), one down GEMM launch, and the two
+chunks' weighted combines.  The per-chunk schedule (every chunk runs permute,
+FFN and combine on its own stream, two streams alternating) is timed beside it.  Inputs are seeded
 synthetic data already resident in HBM when the timed region starts.
 
 Prints ONE JSON line: MoE-layer tokens/s (T / seconds per step), the roofline
@@ -199,8 +200,8 @@ def kernel_times(moe, torch, shape, inp, reps):
         "route_meta": lambda: moe.moe_route_meta(shape, inp["idx"], counts, offsets, splits,
                                                  src_row, dst_row, err, mws, s),
         "permute": lambda: moe.moe_permute(shape, 0, inp["hidden"], dst_row, xp[0], s),
-        "gate_up": lambda: moe.moe_expert_gate_up_pair(shape, 0, xp[0], x1, offsets, inp["wgu"],
-                                                       act, s),
+        "gate_up": lambda: moe.moe_expert_gate_up_gather_pair(shape, 0, inp["hidden"], src_row,
+                                                              offsets, inp["wgu"], act, s),
         "down": lambda: moe.moe_expert_down_pair(shape, 0, act, offsets, inp["wd"], xp[0], x1, s),
         "combine": lambda: moe.moe_unpermute_combine(shape, 0, xp[0], dst_row, inp["w"], out, s),
     }
@@ -345,7 +346,10 @@ def main():
     s = cfg.elem_bytes
     H, I = cfg.H, cfg.I
     A_valid = int(inp["counts"].sum())
-    gu_bytes = rows0 * H * s + e_act0 * 2 * I * H * s + rows0 * I * s
+    # the gate/up launch reads each of the pair's tokens' rows (gathered from
+    # hidden_states), every active expert's weights once, and writes act
+    pair_tokens = min(cfg.T, 2 * -(-cfg.T // N)) if N >= 2 else cfg.T
+    gu_bytes = pair_tokens * H * s + e_act0 * 2 * I * H * s + rows0 * I * s
     gu_flops = 2.0 * rows0 * H * 2 * I
     gu_s = kt["gate_up"] * 1e-6
     peak_f = MFMA_PEAK[cfg.dtype]
@@ -358,8 +362,9 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     traffic = load_traffic(cfg.name, N)
     roof["traffic"] = traffic
-    roof["kernel"] = ("grouped_gemm_bf16<gate_up> (moe_expert_gate_up_pair), chunks 0-1"
-                      if N >= 2 else "grouped_gemm_bf16<gate_up> (moe_expert_gate_up_pair), chunk 0")
+    roof["kernel"] = ("grouped_gemm_bf16<gate_up> (moe_expert_gate_up_gather_pair), chunks 0-1"
+                      if N >= 2 else
+                      "grouped_gemm_bf16<gate_up> (moe_expert_gate_up_gather_pair), chunk 0")
     roof["rows_per_launch"] = rows0
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["algorithmic_flop_per_launch"] = gu_flops
@@ -372,7 +377,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "E": cfg.E, "top_k": cfg.k,
-                   "I": I, "num_chunks": N, "streams": 2, "groups": cfg.groups},
+                   "I": I, "num_chunks": N, "streams": 1, "schedule": "pair_fused",
+                   "groups": cfg.groups},
         "roofline": roof,
         "kernels_us": kt,
         "event_ms_per_step": main_run["event_ms"],

@@ -21,7 +21,7 @@ __all__ = [
     "moe_resolve_num_chunks", "moe_chunk_range", "moe_route_meta_workspace_size",
     "moe_workspace_size", "moe_route_meta", "moe_permute", "moe_expert_gate_up",
     "moe_expert_down", "moe_expert_ffn", "moe_expert_ffn_pair", "moe_expert_gate_up_pair",
-    "moe_expert_down_pair", "moe_unpermute_combine", "moe_chunked_forward",
+    "moe_expert_gate_up_gather_pair", "moe_expert_down_pair", "moe_unpermute_combine", "moe_chunked_forward",
     "moe_chunked_forward_schedule", "moe_backward_workspace_size", "moe_chunked_backward",
     "moe_unpermute_combine_backward", "moe_permute_backward", "MOE_F32", "MOE_BF16",
     "MOE_SCHEDULE_PAIR_FUSED", "MOE_SCHEDULE_PER_CHUNK", "EXPORTED_SYMBOLS",
@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_resolve_num_chunks", "moe_chunk_range",
     "moe_route_meta_workspace_size", "moe_workspace_size", "moe_route_meta", "moe_permute",
     "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_expert_gate_up_pair",
-    "moe_expert_down_pair", "moe_expert_ffn_pair", "moe_unpermute_combine",
+    "moe_expert_gate_up_gather_pair", "moe_expert_down_pair", "moe_expert_ffn_pair", "moe_unpermute_combine",
     "moe_chunked_forward", "moe_chunked_forward_schedule", "moe_backward_workspace_size",
     "moe_chunked_backward", "moe_unpermute_combine_backward", "moe_permute_backward",
 )
@@ -121,6 +121,8 @@ def load_library() -> ctypes.CDLL:
         "moe_expert_ffn": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]),
         "moe_expert_gate_up_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P,
                                                    _P]),
+        "moe_expert_gate_up_gather_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P,
+                                                          _P, _P]),
         "moe_expert_down_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
         "moe_expert_ffn_pair": (ctypes.c_int, [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                                                _P, _P, _P]),
@@ -291,6 +293,18 @@ def moe_expert_gate_up_pair(shape: moe_shape, chunk: int, x_perm0, x_perm1, offs
     _check("moe_expert_gate_up_pair", load_library().moe_expert_gate_up_pair(
         ctypes.byref(shape), chunk, _ptr(x_perm0, dt, rows0 * shape.H, "x_perm0"),
         _ptr(x_perm1, dt, rows1 * shape.H, "x_perm1"),
+        _ptr(offsets, torch.int32, shape.N * (shape.E + 1), "offsets"),
+        _ptr(w_gate_up, dt, shape.E * 2 * shape.I * shape.H, "w_gate_up"),
+        _ptr(act, dt, (rows0 + rows1) * shape.I, "act"), _stream(stream)))
+
+
+def moe_expert_gate_up_gather_pair(shape: moe_shape, chunk: int, hidden_states, src_row, offsets,
+                                   w_gate_up, act, stream=None) -> None:
+    rows0, rows1 = _pair_rows(shape, chunk)
+    dt = shape.torch_dtype
+    _check("moe_expert_gate_up_gather_pair", load_library().moe_expert_gate_up_gather_pair(
+        ctypes.byref(shape), chunk, _ptr(hidden_states, dt, shape.T * shape.H, "hidden_states"),
+        _ptr(src_row, torch.int32, shape.T * shape.k, "src_row"),
         _ptr(offsets, torch.int32, shape.N * (shape.E + 1), "offsets"),
         _ptr(w_gate_up, dt, shape.E * 2 * shape.I * shape.H, "w_gate_up"),
         _ptr(act, dt, (rows0 + rows1) * shape.I, "act"), _stream(stream)))

@@ -407,6 +407,33 @@ moe_status moe_expert_gate_up_pair(const moe_shape* shape, int32_t chunk, const 
   return gate_up(s, io, w_gate_up, stream);
 }
 
+moe_status moe_expert_gate_up_gather_pair(const moe_shape* shape, int32_t chunk,
+                                          const void* hidden_states, const int32_t* src_row,
+                                          const int32_t* offsets, const void* w_gate_up,
+                                          void* act, hipStream_t stream) {
+  Shape s;
+  const int32_t *off0 = nullptr, *off1 = nullptr;
+  int64_t rows0 = 0, rows1 = 0;
+  moe_status st = pair_args(shape, chunk, &s, offsets, &off0, &off1, &rows0, &rows1);
+  if (st != MOE_OK || rows0 + rows1 == 0) return st;
+  if (!buf_ok(hidden_states, 1) || !buf_ok(act, 1) || !buf_ok(w_gate_up, 1) || !src_row ||
+      !aligned(src_row, 4))
+    return MOE_ERR_INVALID_ARG;
+  int t0, t1, u0 = 0, u1 = 0;
+  chunk_tokens(s, chunk, &t0, &t1);
+  if (chunk + 1 < s.N) chunk_tokens(s, chunk + 1, &u0, &u1);
+  GroupedIO io{};
+  io.off[0] = off0;
+  io.off[1] = off1;
+  io.rows_bound = rows0 + rows1;
+  io.a[0] = hidden_states;
+  io.gather[0] = src_row + (size_t)t0 * s.k;
+  io.gather[1] = src_row + (size_t)u0 * s.k;
+  io.gather_k = s.k;
+  io.c[0] = act;
+  return gate_up(s, io, w_gate_up, stream);
+}
+
 moe_status moe_expert_down_pair(const moe_shape* shape, int32_t chunk, const void* act,
                                 const int32_t* offsets, const void* w_down, void* y0, void* y1,
                                 hipStream_t stream) {
@@ -733,8 +760,8 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
   };
 
   if (schedule == MOE_SCHEDULE_PAIR_FUSED) {
-    // Pair (c, c+1): both permutes, one gate_up and one down launch over the
-    // pair's rows, both combines, all on s0.  Every expert's weights are
+    // Pair (c, c+1): one gate_up launch over the pair's rows (gathering them
+    // from hidden_states), one down launch, both combines, all on s0.  Every expert's weights are
     // streamed once per pair.  (Running the second chunk's permute and combine
     // on s1 measured slower: the stream joins cost more than overlapping two
     // memory-bound kernels gains.)
@@ -745,14 +772,30 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
       hipStream_t st1 = s0;
       void* xy0 = w + p.slot[0];
       void* xy1 = p.nslots > 1 ? w + p.slot[1] : nullptr;
-      he = launch_permute(s, t0, t1, hidden_states, dst_row, xy0, s0);
-      if (he == hipSuccess && rows1 > 0)
-        he = launch_permute(s, u0, u1, hidden_states, dst_row, xy1, st1);
-      if (he != hipSuccess) return MOE_ERR_HIP;
       const int32_t* off0 = offsets + (size_t)c * (s.E + 1);
-      // y overwrites the dead x_perm of each slot
-      st = pair_ffn(s, off0, off0 + (s.E + 1), rows0, rows1, xy0, xy1, w_gate_up, w_down,
-                    w + p.slot_act[0], xy0, xy1, s0);
+      // gate_up gathers its rows straight from hidden_states through src_row
+      // (the permute fused into the GEMM's row addressing: same rows, same
+      // bits, no x_perm round trip); down writes y into the slots
+      GroupedIO io{};
+      io.off[0] = off0;
+      io.off[1] = rows1 > 0 ? off0 + (s.E + 1) : nullptr;
+      io.rows_bound = rows0 + rows1;
+      io.a[0] = hidden_states;
+      io.gather[0] = src_row + (size_t)t0 * s.k;
+      io.gather[1] = src_row + (size_t)u0 * s.k;
+      io.gather_k = s.k;
+      io.c[0] = w + p.slot_act[0];
+      st = gate_up(s, io, w_gate_up, s0);
+      if (st != MOE_OK) return st;
+      GroupedIO dn{};
+      dn.off[0] = io.off[0];
+      dn.off[1] = io.off[1];
+      dn.rows_bound = io.rows_bound;
+      dn.a[0] = w + p.slot_act[0];
+      dn.c[0] = xy0;
+      dn.c[1] = xy1;
+      dn.c_split = true;
+      st = down(s, dn, w_down, s0);
       if (st != MOE_OK) return st;
       he = launch_combine(s, t0, t1, xy0, dst_row, top_k_weights, out, s0);
       if (he == hipSuccess && rows1 > 0)

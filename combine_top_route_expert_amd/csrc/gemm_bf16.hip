@@ -75,6 +75,8 @@ struct GemmArgs {
   int lo_rows, hi_rows;       // experts handled by this launch: lo_rows <= rows < hi_rows
   int64_t b_expert_stride;    // elements per expert in B
   uint16_t* gu;               // gate_up, optional: g and u of each row, joint [rows][2I]
+  const int32_t* gather[2];   // optional: A rows gathered from hidden_states (src_row slices)
+  int gather_k;
 };
 
 // Address of virtual row v of the tile's expert on one side of the product.
@@ -138,7 +140,15 @@ struct TileLoader {
       const int row = (wave * LA + t) * G::RPB + row_in_blk;
       const int chunk = slot ^ G::swz(row);
       const int r = row < mrows ? row : mrows - 1;
-      a_src[t] = (const char*)(row_ptr(a.A, a.a_split, tr, tr.v0 + r, a.K) + chunk * 8);
+      if (a.gather[0]) {
+        // permute fused into the row addressing: chunk row -> token
+        int part;
+        const int cr = tr.split_row(tr.v0 + r, &part);
+        const int32_t* src = part ? a.gather[1] : a.gather[0];
+        a_src[t] = (const char*)(a.A[0] + (int64_t)(src[cr] / a.gather_k) * a.K + chunk * 8);
+      } else {
+        a_src[t] = (const char*)(row_ptr(a.A, a.a_split, tr, tr.v0 + r, a.K) + chunk * 8);
+      }
       live_a += (wave * LA + t) * G::RPB < mrows ? 1 : 0;
     }
     const int e = tr.e;
@@ -369,6 +379,9 @@ hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void*
   a.a_split = io.a_split && io.off[1];
   a.c_split = io.c_split && io.off[1];
   a.gu = gate_up ? (uint16_t*)io.gu : nullptr;
+  a.gather[0] = gate_up ? io.gather[0] : nullptr;
+  a.gather[1] = gate_up && io.off[1] ? io.gather[1] : a.gather[0];
+  a.gather_k = io.gather_k;
   a.B = (const uint16_t*)B;
   a.E = s.E;
   a.I = s.I;

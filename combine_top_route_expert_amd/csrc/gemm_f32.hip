@@ -29,6 +29,8 @@ struct GemmArgs {
   int E, K, I, ncols, n_tiles;
   int64_t b_expert_stride;
   float* gu;              // gate_up, optional: g and u of each row, joint [rows][2I]
+  const int32_t* gather[2];  // optional: A rows gathered from hidden_states (src_row slices)
+  int gather_k;
 };
 
 // Address of virtual row v of the tile's expert on one side of the product.
@@ -64,7 +66,15 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_f32(GemmArgs a) {
   // one float4 of A and one of B per thread per stage
   const int lrow = tid >> 2, lk = (tid & 3) * 4;
   const int arow = lrow < mrows ? lrow : mrows - 1;
-  const float* a_src = row_ptr(a.A, a.a_split, tr, tr.v0 + arow, a.K) + lk;
+  const float* a_src;
+  if (a.gather[0]) {  // permute fused into the row addressing: chunk row -> token
+    int part;
+    const int cr = tr.split_row(tr.v0 + arow, &part);
+    const int32_t* src = part ? a.gather[1] : a.gather[0];
+    a_src = a.A[0] + (int64_t)(src[cr] / a.gather_k) * a.K + lk;
+  } else {
+    a_src = row_ptr(a.A, a.a_split, tr, tr.v0 + arow, a.K) + lk;
+  }
   int brow;
   if constexpr (kGateUp) {
     const int i = nt * 32 + (lrow & 31);
@@ -154,6 +164,9 @@ hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void*
   a.a_split = io.a_split && io.off[1];
   a.c_split = io.c_split && io.off[1];
   a.gu = gate_up ? (float*)io.gu : nullptr;
+  a.gather[0] = gate_up ? io.gather[0] : nullptr;
+  a.gather[1] = gate_up && io.off[1] ? io.gather[1] : a.gather[0];
+  a.gather_k = io.gather_k;
   a.B = (const float*)B;
   a.E = s.E;
   a.I = s.I;

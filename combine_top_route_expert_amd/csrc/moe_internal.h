@@ -67,6 +67,11 @@ struct GroupedIO {
   bool a_split, c_split;
   int64_t rows_bound;    // total rows of the launch (host-known bound)
   void* gu = nullptr;    // gate_up only, optional: joint [rows][2I] copy of g and u
+  // Gather (gate_up only, optional): A is hidden_states [T][K] (a[0]) and row r
+  // of chunk part p is token gather[p][r] / k -- the permute fused into the
+  // GEMM's row addressing (gather[p] = the chunk's slice of src_row).
+  const int32_t* gather[2] = {nullptr, nullptr};
+  int gather_k = 0;
 };
 
 // Backward products (gemm_bwd_bf16.hip, gemm_bwd_f32.hip).  Rows follow the

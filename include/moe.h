@@ -200,6 +200,18 @@ moe_status moe_expert_gate_up_pair(const moe_shape* shape, int32_t chunk, const 
                                    const void* x_perm1, const int32_t* offsets,
                                    const void* w_gate_up, void* act, hipStream_t stream);
 
+/*
+ * moe_expert_gate_up_pair with the permute fused into the GEMM's row addressing
+ * (what moe_chunked_forward's pair-fused schedule runs): row r of chunk c is
+ * read straight from hidden_states[src_row[t0_c*k + r] / k] instead of from an
+ * x_perm buffer.  src_row is the full [T*k] array from moe_route_meta; act as
+ * for moe_expert_gate_up_pair.  Same bits as permute + moe_expert_gate_up_pair.
+ */
+moe_status moe_expert_gate_up_gather_pair(const moe_shape* shape, int32_t chunk,
+                                          const void* hidden_states, const int32_t* src_row,
+                                          const int32_t* offsets, const void* w_gate_up,
+                                          void* act, hipStream_t stream);
+
 moe_status moe_expert_down_pair(const moe_shape* shape, int32_t chunk, const void* act,
                                 const int32_t* offsets, const void* w_down, void* y0, void* y1,
                                 hipStream_t stream);
@@ -230,10 +242,12 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  * Metadata for all chunks runs once on s0.  Adjacent chunks (0,1), (2,3), ...
  * form pairs; at most two chunks are resident (workspace slots 0 and 1), and a
  * last odd chunk runs alone.
- *  MOE_SCHEDULE_PAIR_FUSED: both permutes of the pair, one gate_up and one down
- *    launch over the pair's rows (moe_expert_ffn_pair), both combines, all on
- *    s0 (s1 is not used: on MI355X the joins that would let the second chunk's
- *    permute and combine overlap on s1 cost more than the overlap gains).
+ *  MOE_SCHEDULE_PAIR_FUSED: one gate_up launch over the pair's rows, which
+ *    gathers each row straight from hidden_states through src_row (the permute
+ *    fused into the GEMM's row addressing: same rows, same bits, no x_perm
+ *    buffer traffic), one down launch, both combines, all on s0 (s1 is not
+ *    used: on MI355X the joins that would let the second chunk's steps overlap
+ *    on s1 cost more than the overlap gains).
  *  MOE_SCHEDULE_PER_CHUNK: chunk c runs permute -> gate_up -> down -> combine on
  *    stream s[c % 2] in slot c % 2, so the two chunks of a pair overlap as whole
  *    pipelines; every chunk streams the expert weights again.

@@ -298,6 +298,13 @@ def test_expert_ffn_pair_bitwise(name, N, c):
         if n1:
             assert torch.equal(act[b + n0:b + n0 + n1], ref_act[c + 1][int(o1[e]):int(o1[e]) + n1]), e
     assert bool((act[valid0 + valid1:] == 555.0).all())
+    # the gate_up with the permute fused (rows gathered from hidden_states)
+    src = torch.from_numpy(meta["src_row"]).cuda()
+    act2 = torch.full_like(act, 555.0)
+    say(f"gate_up_gather_pair {name} N={N} chunk={c}")
+    moe.moe_expert_gate_up_gather_pair(shape, c, L.hidden, src, off, L.wgu, act2)
+    torch.cuda.synchronize()
+    assert torch.equal(act2, act)
 
 
 def test_run_twice_identical():
