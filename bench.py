@@ -31,16 +31,26 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/s (permute+expert GEMM+combine); % HBM / % MFMA peak"
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense FLOP/s (fp32: matrix/vector peak)
-GATE_UP_SRC = os.path.join(ROOT, "combine_top_route_expert_amd", "csrc", "gemm_bf16.hip")
+GATE_UP_SRCS = tuple(os.path.join(ROOT, "combine_top_route_expert_amd", "csrc", f)
+                     for f in ("gemm_bf16.hip", "moe_internal.h"))
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths=GATE_UP_SRCS):
+    """Hash of the code the gate/up kernel is built from, comments and blank
+    space dropped, so that an edit of a comment keeps the recorded counters."""
+    import re
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def make_inputs(cfg, torch, synth):
@@ -245,7 +255,7 @@ def load_traffic(config_name, N):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != source_sha(GATE_UP_SRC):
+    if d.get("kernel_source_sha256_16") != source_sha():
         return None
     return d.get("hbm_bytes_per_launch")
 

@@ -47,7 +47,9 @@
 // 1.5-2.1 GHz) and a full 256 x 256 tile takes ~1.45x the cycles of its MFMAs.
 // Deeper pipelines (BK 32 with 4-5 stages, a third weight buffer),
 // register-staged loads, loads interleaved with the MFMAs, round-robin XCD
-// dealing and 4-wave 128 x 128 wave tiles all measured no faster.
+// dealing and 4-wave 128 x 128 wave tiles all measured no faster.  What did
+// help (5-12% on the larger workloads): a K loop whose body holds no branch,
+// with the wave's count of live 32-row blocks chosen once before the loop.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -250,13 +252,53 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
     }
 }
 
+// The K loop of one wave.  F (<= FM) 32-row blocks of the wave's band take
+// part in the MFMAs (F = 0: none); the wave still issues its share of every
+// stage's loads and joins every barrier.  The loop body holds no branch, so
+// the compiler schedules the fragment reads, MFMAs and the next stage's loads
+// as one block.
+template <int F, int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, class Loader>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
+                                       int KT, int per_stage, int lane, int wm, int wn) {
+  using G = StageGeom<BK>;
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt has landed once only the newer stages issued so far are pending
+    const int newer = KT - 1 - kt < STAGES - 2 ? KT - 1 - kt : STAGES - 2;
+    wait_loads(newer * per_stage);
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    const char* sa = smem + (kt % STAGES) * Loader::STAGE_BYTES;
+    const char* sb = sa + BM * G::ROW_BYTES;
+    if constexpr (F > 0) {
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int fo = G::frag_offset(lane, kk);
+        bf16x8 af[F], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+          af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    // this stage's LDS reads are complete before any wave refills its buffer
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+}
+
 template <bool kGateUp, int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(GemmArgs a) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   using Loader = TileLoader<kGateUp, BM, BN, NW, WN, BK>;
-  using G = StageGeom<BK>;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(!kGateUp || WN % 64 == 0, "gate/up halves");
   static_assert(STAGES >= 2, "pipeline depth");
@@ -281,42 +323,31 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
   const int KT = a.K / BK;
-  // a wave whose rows all lie past the tile's rows has no MFMA work
-  const bool rows_live = wm * WM < tr.rows;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) ld.issue(smem, s, s);
-
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage kt has landed once only the newer stages issued so far are pending
-    const int newer = KT - 1 - kt < STAGES - 2 ? KT - 1 - kt : STAGES - 2;
-    wait_loads(newer * per_stage);
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const char* sa = smem + (kt % STAGES) * Loader::STAGE_BYTES;
-    const char* sb = sa + BM * G::ROW_BYTES;
-    if (rows_live) {
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int fo = G::frag_offset(lane, kk);
-        bf16x8 af[FM], bfr[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * G::ROW_BYTES + fo);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    // this stage's LDS reads are complete before any wave refills its buffer
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  // 32-row blocks of this wave's band that hold rows of the tile.  Blocks past
+  // them feed only outputs that are never stored, so a wide tile skips their
+  // MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block loop, 3 runs
+  // the full one).  A one-block band always runs its MFMAs: a wave-uniform
+  // branch there measured slower than the wasted work.
+  const int band_rows = tr.rows - wm * WM;
+  const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
+#define MOE_K_LOOP(F) \
+  k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
+  if constexpr (FM == 1) {
+    MOE_K_LOOP(1);
+  } else {
+    if (fm_live > 2)
+      MOE_K_LOOP(FM);
+    else if (fm_live == 2)
+      MOE_K_LOOP(2);
+    else if (fm_live == 1)
+      MOE_K_LOOP(1);
+    else
+      MOE_K_LOOP(0);
   }
+#undef MOE_K_LOOP
   store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
 }
 

@@ -26,6 +26,8 @@
 // round-robin (xcd_tile_rr), and the K loop runs over the expert's rows of both
 // chunks; rows past the expert's block are loaded from a
 // clamped row and zeroed in the A fragment.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -227,35 +229,52 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
   const int KT = a.K / BK;
-  const bool rows_live = wm * WM < tr.rows;
-  issue(0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    __builtin_amdgcn_s_barrier();
-    if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
-    const char* sa = smem + (kt & 1) * STAGE;
-    const char* sb = sa + A_BYTES;
-    if (rows_live) {
+  // F (<= FM) 32-row blocks of the wave's band take part in the MFMAs; the
+  // loop body holds no branch (as in the forward grouped GEMM)
+  auto k_loop = [&](auto f_const) {
+    constexpr int F = decltype(f_const)::value;
+    issue(0, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      __builtin_amdgcn_s_barrier();
+      if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
+      const char* sa = smem + (kt & 1) * STAGE;
+      const char* sb = sa + A_BYTES;
+      if constexpr (F > 0) {
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int fo = kfrag_offset(lane, kk);
-        bf16x8 af[FM], bfr[FN];
+        for (int kk = 0; kk < BK / 16; ++kk) {
+          const int fo = kfrag_offset(lane, kk);
+          bf16x8 af[F], bfr[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * 128 + fo);
+          for (int i = 0; i < F; ++i)
+            af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * 128 + fo);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int cb = wn * WN + j * 32;
-          bfr[j] = tr_frag(sb, GB::tr_offset(lane, cb, kk, 0), GB::tr_offset(lane, cb, kk, 1));
+          for (int j = 0; j < FN; ++j) {
+            const int cb = wn * WN + j * 32;
+            bfr[j] = tr_frag(sb, GB::tr_offset(lane, cb, kk, 0), GB::tr_offset(lane, cb, kk, 1));
+          }
+#pragma unroll
+          for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  }
+  };
+  const int band_rows = tr.rows - wm * WM;
+  const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
+  static_assert(FM == 4, "band dispatch below assumes four 32-row blocks per wave");
+  if (fm_live > 2)
+    k_loop(std::integral_constant<int, FM>{});
+  else if (fm_live == 2)
+    k_loop(std::integral_constant<int, 2>{});
+  else if (fm_live == 1)
+    k_loop(std::integral_constant<int, 1>{});
+  else
+    k_loop(std::integral_constant<int, 0>{});
 
   // epilogue: lane l holds column l % 32 of rows 8(q/4) + 4(l/32) + q%4 of each block
   const int rbase = wm * WM + 4 * (lane >> 5);
