@@ -32,11 +32,13 @@
 // accumulators of the same (row, i) and SwiGLU runs in registers: no
 // [rows][2I] intermediate is written.
 //
-// Grouping: m-tiles of all experts are numbered expert by expert; every
-// workgroup builds that numbering from the device-resident offsets (MTileMap),
-// so the host never reads group sizes.  Each XCD takes a contiguous range of
-// m-tiles with all their n-tiles (xcd_tile).  The grid is bounded from the
-// launch's assignment count and surplus workgroups exit.  Rows past an
+// Grouping: every workgroup numbers the m-tiles of all experts from the
+// device-resident offsets (MTileMap: full m-tiles first, then the partial ones
+// by size class), so the host never reads group sizes.  Each XCD takes a
+// contiguous range of the full m-tiles and a round-robin share of the partial
+// ones, each with all its n-tiles (xcd_tile), so it runs its longest tiles
+// first.  The grid is bounded from the launch's assignment count and surplus
+// workgroups exit.  Rows past an
 // expert's block are loaded from a clamped row (A blocks wholly past it are
 // not loaded at all) and never stored.
 //
@@ -74,7 +76,6 @@ struct GemmArgs {
   const int32_t* off1;        // E + 1 offsets of the pair's second chunk, or null
   int a_split, c_split;
   int E, K, I, ncols, n_tiles;
-  int lo_rows, hi_rows;       // experts handled by this launch: lo_rows <= rows < hi_rows
   int64_t b_expert_stride;    // elements per expert in B
   uint16_t* gu;               // gate_up, optional: g and u of each row, joint [rows][2I]
   const int32_t* gather[2];   // optional: A rows gathered from hidden_states (src_row slices)
@@ -308,9 +309,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   MTileMap tm;
-  tm.build(a.off0, a.off1, a.E, BM, a.lo_rows, a.hi_rows);
+  // the wide tile (one workgroup per CU) orders small experts' m-tiles by size
+  // to balance the XCDs; the narrow tile (three per CU) keeps expert order,
+  // which mixes weight-streaming and MFMA-bound tiles on a CU (measured faster)
+  tm.build(a.off0, a.off1, a.E, BM, BM >= 128 ? BM : 1);
   int mt, nt;
-  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  if (!xcd_tile(tm, a.n_tiles, &mt, &nt)) return;
   const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
   Loader ld;
   ld.init(a, tr, nt, lane, wave);
@@ -373,8 +377,6 @@ hipError_t launch_instance(GemmArgs a, const Shape& s, int64_t rows_bound, hipSt
   constexpr int threads = 64 * WM_ * WN_;
   // gate_up tiles cover BN/2 intermediate columns (gate and up halves)
   a.n_tiles = kGateUp ? s.I / (BN / 2) : (s.H + BN - 1) / BN;
-  a.lo_rows = 1;
-  a.hi_rows = 0x7fffffff;
   const int64_t grid = xcd_grid(m_tiles_bound(rows_bound, s.E, BM), a.n_tiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -105,15 +105,6 @@ __device__ __forceinline__ uint64_t side_addr(const SideU& s, const TileRows& tr
   return s.b0 + shift + (uint64_t)(row * s.ld + col) * 2u;
 }
 
-__device__ __forceinline__ const uint16_t* side_row(const Side& s, const TileRows& tr, int v) {
-  if (s.split) {
-    int part;
-    const int r = tr.split_row(v, &part);
-    return (part ? s.p[1] : s.p[0]) + (int64_t)r * s.ld;
-  }
-  return s.p[0] + (int64_t)tr.joint_row(v) * s.ld;
-}
-
 // ---- LDS layouts --------------------------------------------------------------
 // K-contiguous rows (dgrad A): BM rows x 128 bytes per stage, chunk c of row r at
 // slot c ^ ((r >> 1) & 7) (same as the forward kernels).
@@ -181,20 +172,21 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   MTileMap tm;
-  tm.build(a.off0, a.off1, a.E, BM);
+  tm.build(a.off0, a.off1, a.E, BM, BM);
   int mt, nt;
-  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  if (!xcd_tile(tm, a.n_tiles, &mt, &nt)) return;
   const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
 
   // A: lane l of block b holds tile row 8b + l/8, 16-byte slot l % 8
   const char* a_src[LA];
   int live_a = 0;
+  const SideU a_u = uniform_side(a.a);
 #pragma unroll
   for (int t = 0; t < LA; ++t) {
     const int row = (wave * LA + t) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     const int r = row < tr.rows ? row : tr.rows - 1;
-    a_src[t] = (const char*)(side_row(a.a, tr, tr.v0 + r) + chunk * 8);
+    a_src[t] = (const char*)side_addr(a_u, tr, tr.v0 + r, chunk * 8);
     live_a += (wave * LA + t) * 8 < tr.rows ? 1 : 0;
   }
   // B: lane l of block b holds K row ROWS_PER_KB*b + l/SLOTS, slot l % SLOTS
@@ -531,8 +523,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
     }
 }
 
-int64_t grid_of(int64_t m_bound, int n_tiles) { return xcd_grid(m_bound, n_tiles); }
-
 }  // namespace
 
 hipError_t launch_dgrad_bf16(const Shape& s, const DgradIO& io, hipStream_t st) {
@@ -556,7 +546,7 @@ hipError_t launch_dgrad_bf16(const Shape& s, const DgradIO& io, hipStream_t st) 
   a.I = s.I;
   constexpr int BM = 256, BN = 256;
   a.n_tiles = (io.N + BN - 1) / BN;
-  const int64_t grid = grid_of(m_tiles_bound(io.rows_bound, s.E, BM), a.n_tiles);
+  const int64_t grid = xcd_grid(m_tiles_bound(io.rows_bound, s.E, BM), a.n_tiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (io.gu)
@@ -588,7 +578,7 @@ hipError_t launch_wgrad_bf16(const Shape& s, const WgradIO& io, hipStream_t st) 
   constexpr int BM = 256, BN = 256;
   a.m_tiles = (io.M + BM - 1) / BM;
   a.n_tiles = (io.N + BN - 1) / BN;
-  const int64_t grid = grid_of((int64_t)s.E * a.m_tiles, a.n_tiles);
+  const int64_t grid = xcd_grid_rr((int64_t)s.E * a.m_tiles, a.n_tiles);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((wgrad_gemm_bf16<BM, BN, 2, 4>), dim3((unsigned)grid), dim3(512), 0, st, a);
   return hipGetLastError();

@@ -46,9 +46,9 @@ __global__ void __launch_bounds__(kThreads) dgrad_gemm_f32(DgradArgsF a) {
   __shared__ float Bs[BKF][BN];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   MTileMap tm;
-  tm.build(a.off0, a.off1, a.E, BM);
+  tm.build(a.off0, a.off1, a.E, BM, 1);
   int mt, nt;
-  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  if (!xcd_tile(tm, a.n_tiles, &mt, &nt)) return;
   const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
   const float* Be = a.B + (int64_t)tr.e * a.K * a.N;
 
@@ -224,7 +224,7 @@ hipError_t launch_wgrad_f32(const Shape& s, const WgradIO& io, hipStream_t st) {
   a.accumulate = io.accumulate;
   a.m_tiles = (io.M + BM - 1) / BM;
   a.n_tiles = (io.N + BN - 1) / BN;
-  const int64_t grid = xcd_grid((int64_t)s.E * a.m_tiles, a.n_tiles);
+  const int64_t grid = xcd_grid_rr((int64_t)s.E * a.m_tiles, a.n_tiles);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(wgrad_gemm_f32, dim3((unsigned)grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();

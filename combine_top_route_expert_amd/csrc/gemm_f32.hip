@@ -57,9 +57,9 @@ __global__ void __launch_bounds__(kThreads) grouped_gemm_f32(GemmArgs a) {
   __shared__ float Bs[BN][BK + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   MTileMap tm;
-  tm.build(a.off0, a.off1, a.E, BM);
+  tm.build(a.off0, a.off1, a.E, BM, 1);
   int mt, nt;
-  if (!xcd_tile(tm.total, a.n_tiles, &mt, &nt)) return;
+  if (!xcd_tile(tm, a.n_tiles, &mt, &nt)) return;
   const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
   const int e = tr.e, mrows = tr.rows;
 

@@ -134,19 +134,25 @@ struct TileRows {
 };
 
 // Grouped-GEMM tile map.  Expert e owns n_e rows (its rows in one or two
-// chunks) and ceil(n_e / BM) m-tiles; m-tiles are numbered expert by expert.
-// A map can be restricted to a class of experts by row count, so that one
-// launch covers long expert blocks with a large tile and another the short
-// ones.  Every wave of a workgroup builds the map independently (one wave scan
+// chunks) and ceil(n_e / BM) m-tiles.  Numbering: first the m-tiles of the
+// large experts (n_e >= large_min), expert by expert; then the single m-tile
+// of each small expert (0 < n_e < large_min <= BM), in four size classes,
+// larger first: more than BM/2 rows, more than BM/4, more than BM/8, the rest
+// (each class expert by expert).  large_min = 1 gives plain expert order.  Every wave of a workgroup builds the map independently (wave scans
 // over E experts, E/64 per lane) and gets the same answer.
 struct MTileMap {
-  int total;              // m-tiles of all experts in the class
-  int excl, incl;         // this lane's m-tile range
-  int e_begin, e_end;     // this lane's experts
-  int lo_rows, hi_rows;   // class: experts with lo_rows <= rows < hi_rows
+  static constexpr int kClasses = 5;  // 0: large experts' m-tiles; 1..4: small experts by size
+  int total;                // m-tiles
+  int large;                // m-tiles of large experts (numbers 0 .. large-1)
+  int start[kClasses + 1];  // first number of each class; start[kClasses] = total
+  int large_min;            // rows that make an expert large
+  int excl_large, incl_large;   // this lane's range of large-expert m-tiles
+  int excl_small[2], incl_small[2];  // this lane's range within classes 1|2 and
+                                     // 3|4, 16 bits per class (E < 65536)
+  int e_begin, e_end;       // this lane's experts
 
-  __device__ __forceinline__ int tiles_of(int n, int BM) const {
-    return (n >= lo_rows && n < hi_rows) ? (n + BM - 1) / BM : 0;
+  static __device__ __forceinline__ int small_class(int n, int BM) {
+    return n > BM / 2 ? 1 : n > BM / 4 ? 2 : n > BM / 8 ? 3 : 4;
   }
 
   static __device__ __forceinline__ int rows_of(const int32_t* __restrict__ off0,
@@ -156,24 +162,49 @@ struct MTileMap {
     return n;
   }
 
+  static __device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = __lane_id();
+    for (int d = 1; d < 64; d <<= 1) {
+      const int n = __shfl_up(v, d);
+      if (lane >= d) v += n;
+    }
+    return v;
+  }
+
   __device__ __forceinline__ void build(const int32_t* __restrict__ off0,
                                         const int32_t* __restrict__ off1, int E, int BM,
-                                        int lo = 1, int hi = 0x7fffffff) {
-    lo_rows = lo;
-    hi_rows = hi;
+                                        int large_rows) {
+    large_min = large_rows;
     const int lane = __lane_id();
     const int per = (E + 63) >> 6;
     e_begin = lane * per;
     e_end = e_begin + per < E ? e_begin + per : E;
-    int sum = 0;
-    for (int e = e_begin; e < e_end; ++e) sum += tiles_of(rows_of(off0, off1, e), BM);
-    incl = sum;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int n = __shfl_up(incl, d);
-      if (lane >= d) incl += n;
+    int nl = 0, p12 = 0, p34 = 0;  // small-expert counts: classes 1|2 and 3|4, 16 bits each
+    for (int e = e_begin; e < e_end; ++e) {
+      const int n = rows_of(off0, off1, e);
+      if (n >= large_min) {
+        nl += (n + BM - 1) / BM;
+      } else if (n > 0) {
+        const int c = small_class(n, BM);
+        const int add = 1 << (16 * ((c - 1) & 1));
+        if (c <= 2) p12 += add; else p34 += add;
+      }
     }
-    excl = incl - sum;
-    total = __shfl(incl, 63);
+    incl_large = wave_incl_scan(nl);
+    excl_large = incl_large - nl;
+    incl_small[0] = wave_incl_scan(p12);
+    incl_small[1] = wave_incl_scan(p34);
+    excl_small[0] = incl_small[0] - p12;
+    excl_small[1] = incl_small[1] - p34;
+    large = __shfl(incl_large, 63);
+    const int t12 = __shfl(incl_small[0], 63), t34 = __shfl(incl_small[1], 63);
+    start[0] = 0;
+    start[1] = large;
+    start[2] = start[1] + (t12 & 0xFFFF);
+    start[3] = start[2] + (t12 >> 16);
+    start[4] = start[3] + (t34 & 0xFFFF);
+    start[5] = start[4] + (t34 >> 16);
+    total = start[5];
   }
 
   // Rows of m-tile mt (< total), for all lanes.
@@ -181,24 +212,60 @@ struct MTileMap {
                                              const int32_t* __restrict__ off1, int BM,
                                              int mt) const {
     const int lane = __lane_id();
-    const uint64_t own = __ballot(excl <= mt && mt < incl);
+    // class and range by selects only (no dynamic indexing, which would put
+    // the arrays in scratch memory)
+    int cls = 0, base = 0;
+#pragma unroll
+    for (int c = 1; c < kClasses; ++c)
+      if (mt >= start[c]) {
+        cls = c;
+        base = start[c];
+      }
+    const int local = mt - base;
+    int lo, hi;
+    if (cls == 0) {
+      lo = excl_large;
+      hi = incl_large;
+    } else {
+      const int sh = 16 * ((cls - 1) & 1);
+      const int ex = cls <= 2 ? excl_small[0] : excl_small[1];
+      const int in = cls <= 2 ? incl_small[0] : incl_small[1];
+      lo = (ex >> sh) & 0xFFFF;
+      hi = (in >> sh) & 0xFFFF;
+    }
+    const uint64_t own = __ballot(lo <= local && local < hi);
     const int owner = __ffsll((unsigned long long)own) - 1;
     int fe = 0, fv0 = 0, frows = 0, flo0 = 0, fn0 = 0, flo1 = 0;
     if (lane == owner) {
-      int acc = excl;
+      int acc = lo;
       for (int e = e_begin; e < e_end; ++e) {
         const int n = rows_of(off0, off1, e);
-        const int t = tiles_of(n, BM);
-        if (mt < acc + t) {
+        bool hit = false;
+        if (cls == 0) {
+          if (n >= large_min) {
+            const int t = (n + BM - 1) / BM;
+            if (local < acc + t) {
+              hit = true;
+              fv0 = (local - acc) * BM;
+              frows = n - fv0 < BM ? n - fv0 : BM;
+            }
+            acc += t;
+          }
+        } else if (n > 0 && n < large_min && small_class(n, BM) == cls) {
+          if (local == acc) {
+            hit = true;
+            fv0 = 0;
+            frows = n;
+          }
+          ++acc;
+        }
+        if (hit) {
           fe = e;
-          fv0 = (mt - acc) * BM;
-          frows = n - fv0 < BM ? n - fv0 : BM;
           flo0 = off0[e];
           fn0 = off0[e + 1] - flo0;
           flo1 = off1 ? off1[e] : 0;
           break;
         }
-        acc += t;
       }
     }
     TileRows r;
@@ -212,28 +279,43 @@ struct MTileMap {
   }
 };
 
-// Workgroup -> (m-tile, n-tile).  Workgroup b runs on XCD b % 8 (checked
-// against the hardware XCC id); each XCD gets a contiguous range of
-// ceil(total/8) m-tiles with all their n-tiles, in order, so an m-tile's
-// activation panel and an expert's weight panels are fetched into one XCD's L2
-// instead of up to eight (dealing m-tiles round-robin balances the XCDs better
-// but measured no faster: each tile then misses more).  The grid has
-// 8 * ceil(bound/8) * n_tiles workgroups; those past their XCD's range exit.
-__device__ __forceinline__ bool xcd_tile(int total, int n_tiles, int* mt, int* nt) {
+// Workgroup -> (m-tile, n-tile) for an MTileMap.  Workgroup b runs on XCD
+// b % 8 (checked against the hardware XCC id), and an XCD starts its
+// workgroups in order of b.  XCD x first takes a contiguous range of the
+// large experts' m-tiles (ceil(large/8) per XCD, fewer for the last ones), so
+// an m-tile's activation panel and an expert's weight panels are fetched into
+// one XCD's L2.  The small experts' m-tiles, larger first, then fill the XCDs
+// that got fewer large m-tiles up to ceil(large/8), and the rest are dealt
+// round-robin.  Every m-tile comes with all its n-tiles.  So every XCD gets
+// ceil(total/8) or fewer m-tiles, the work is spread evenly, and each XCD runs
+// its longest tiles first, which shortens the tail of the launch.  The grid
+// has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid); those past their
+// XCD's share exit.
+__device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* mt, int* nt) {
   const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
-  const int per = (total + 7) >> 3;
   const int ml = q / n_tiles;
-  if (ml >= per) return false;
-  *mt = x * per + ml;
   *nt = q - ml * n_tiles;
-  return *mt < total;
+  const int per = (tm.large + 7) >> 3;
+  int nl = tm.large - x * per;  // large-expert m-tiles of this XCD
+  nl = nl < 0 ? 0 : nl > per ? per : nl;
+  if (ml < nl) {
+    *mt = x * per + ml;
+    return true;
+  }
+  const int j = ml - nl;                    // this XCD's j-th small-expert m-tile
+  const int deficit = per - nl;             // slots left below `per` on this XCD
+  int before = x * per - tm.large;          // slots left on the XCDs before it
+  before = before < 0 ? 0 : before;
+  const int p = j < deficit ? before + j : (8 * per - tm.large) + (j - deficit) * 8 + x;
+  *mt = tm.large + p;
+  return *mt < tm.total;
 }
 
 // Round-robin variant: XCD x takes m-tiles x, x + 8, x + 16, ... (each with all
 // its n-tiles).  For the weight-gradient products, whose m-tiles are (expert,
 // row block) pairs with a reduction as long as the expert's row count, this
 // spreads each heavily loaded expert over all eight XCDs instead of queueing
-// it on one.  Same grid as xcd_tile.
+// it on one.  Grid: xcd_grid_rr.
 __device__ __forceinline__ bool xcd_tile_rr(int total, int n_tiles, int* mt, int* nt) {
   const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int ml = q / n_tiles;
@@ -242,9 +324,15 @@ __device__ __forceinline__ bool xcd_tile_rr(int total, int n_tiles, int* mt, int
   return *mt < total;
 }
 
-// Host side: grid of xcd_tile for a bound on the m-tiles.
+// Host side: grid of xcd_tile for a bound on the m-tiles (no XCD gets more
+// than ceil(total/8) of them).
 inline int64_t xcd_grid(int64_t m_tiles_bound, int n_tiles) {
   return 8 * ((m_tiles_bound + 7) / 8) * (int64_t)n_tiles;
+}
+
+// Host side: grid of xcd_tile_rr for exactly m_tiles m-tiles.
+inline int64_t xcd_grid_rr(int64_t m_tiles, int n_tiles) {
+  return 8 * ((m_tiles + 7) / 8) * (int64_t)n_tiles;
 }
 
 // Upper bound on the m-tiles of a grouped GEMM over `rows` rows split among E
