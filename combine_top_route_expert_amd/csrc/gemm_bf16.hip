@@ -33,14 +33,13 @@
 // [rows][2I] intermediate is written.
 //
 // Grouping: every workgroup numbers the m-tiles of all experts from the
-// device-resident offsets (MTileMap: full m-tiles first, then the partial ones
-// by size class), so the host never reads group sizes.  Each XCD takes a
-// contiguous range of the full m-tiles and a round-robin share of the partial
-// ones, each with all its n-tiles (xcd_tile), so it runs its longest tiles
-// first.  The grid is bounded from the launch's assignment count and surplus
-// workgroups exit.  Rows past an
-// expert's block are loaded from a clamped row (A blocks wholly past it are
-// not loaded at all) and never stored.
+// device-resident offsets (MTileMap: the large experts' m-tiles first, then
+// the small experts' by size class), so the host never reads group sizes.
+// Each XCD takes a contiguous range of the large experts' m-tiles and an even
+// share of the small ones, interleaved, each with all its n-tiles (xcd_tile).
+// The grid is bounded from the launch's assignment count and surplus
+// workgroups exit.  Rows past an expert's block are loaded from a clamped row
+// (A blocks wholly past it are not loaded at all) and never stored.
 //
 // What bounds it (measured with per-workgroup timestamps): the MFMA loop alone
 // (no global loads) runs at ~94% of the matrix peak at the clock it gets, and

@@ -138,8 +138,9 @@ struct TileRows {
 // large experts (n_e >= large_min), expert by expert; then the single m-tile
 // of each small expert (0 < n_e < large_min <= BM), in four size classes,
 // larger first: more than BM/2 rows, more than BM/4, more than BM/8, the rest
-// (each class expert by expert).  large_min = 1 gives plain expert order.  Every wave of a workgroup builds the map independently (wave scans
-// over E experts, E/64 per lane) and gets the same answer.
+// (each class expert by expert).  large_min = 1 gives plain expert order.
+// Every wave of a workgroup builds the map independently (wave scans over E
+// experts, E/64 per lane) and gets the same answer.
 struct MTileMap {
   static constexpr int kClasses = 5;  // 0: large experts' m-tiles; 1..4: small experts by size
   int total;                // m-tiles
@@ -281,16 +282,19 @@ struct MTileMap {
 
 // Workgroup -> (m-tile, n-tile) for an MTileMap.  Workgroup b runs on XCD
 // b % 8 (checked against the hardware XCC id), and an XCD starts its
-// workgroups in order of b.  XCD x first takes a contiguous range of the
-// large experts' m-tiles (ceil(large/8) per XCD, fewer for the last ones), so
-// an m-tile's activation panel and an expert's weight panels are fetched into
-// one XCD's L2.  The small experts' m-tiles, larger first, then fill the XCDs
-// that got fewer large m-tiles up to ceil(large/8), and the rest are dealt
-// round-robin.  Every m-tile comes with all its n-tiles.  So every XCD gets
-// ceil(total/8) or fewer m-tiles, the work is spread evenly, and each XCD runs
-// its longest tiles first, which shortens the tail of the launch.  The grid
-// has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid); those past their
-// XCD's share exit.
+// workgroups in order of b.  Which m-tiles an XCD gets: a contiguous range of
+// the large experts' m-tiles (ceil(large/8) per XCD, fewer for the last
+// ones), so an expert's weight panels are fetched into one XCD's L2; then the
+// small experts' m-tiles (larger first) top up the XCDs that got fewer large
+// ones to ceil(large/8), and the rest are dealt round-robin.  So no XCD gets
+// more than ceil(total/8) m-tiles and the work is spread evenly.  In which
+// order: the XCD's large and small m-tiles are interleaved evenly, so that
+// MFMA-bound large tiles and weight-streaming small tiles run side by side
+// (small tiles started all together contend for HBM), except that its last
+// ceil(32/n_tiles) m-tiles (about one workgroup per CU) are its smallest ones,
+// which shortens the tail of the launch.  Every m-tile comes with all its
+// n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
+// those past their XCD's share exit.
 __device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* mt, int* nt) {
   const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int ml = q / n_tiles;
@@ -298,15 +302,31 @@ __device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* m
   const int per = (tm.large + 7) >> 3;
   int nl = tm.large - x * per;  // large-expert m-tiles of this XCD
   nl = nl < 0 ? 0 : nl > per ? per : nl;
-  if (ml < nl) {
-    *mt = x * per + ml;
-    return true;
-  }
-  const int j = ml - nl;                    // this XCD's j-th small-expert m-tile
-  const int deficit = per - nl;             // slots left below `per` on this XCD
-  int before = x * per - tm.large;          // slots left on the XCDs before it
+  const int S = tm.total - tm.large;  // small-expert m-tiles, numbered p = 0 .. S-1
+  const int D = 8 * per - tm.large;   // slots below `per` over all XCDs
+  const int deficit = per - nl;       // this XCD's slots below `per`
+  int before = x * per - tm.large;    // slots below `per` on the XCDs before it
   before = before < 0 ? 0 : before;
-  const int p = j < deficit ? before + j : (8 * per - tm.large) + (j - deficit) * 8 + x;
+  int ns = S - before < 0 ? 0 : S - before;  // this XCD's small m-tiles
+  ns = ns < deficit ? ns : deficit;
+  if (S > D + x) ns += (S - D - x + 7) / 8;
+  const int C = nl + ns;
+  if (ml >= C) return false;
+  int R = (32 + n_tiles - 1) / n_tiles;  // small m-tiles kept for the end
+  R = R < ns ? R : ns;
+  const int C1 = C - R;                  // positions of the even interleave
+  int j;                                 // this XCD's j-th small m-tile
+  if (ml >= C1) {
+    j = ns - R + (ml - C1);
+  } else {
+    const int lb = (int)((long long)ml * nl / C1), la = (int)((long long)(ml + 1) * nl / C1);
+    if (la > lb) {
+      *mt = x * per + lb;
+      return true;
+    }
+    j = ml - lb;
+  }
+  const int p = j < deficit ? before + j : D + (j - deficit) * 8 + x;
   *mt = tm.large + p;
   return *mt < tm.total;
 }
