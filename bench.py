@@ -331,9 +331,15 @@ def main():
     inp = make_inputs(cfg, torch, synth)
     shape = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, N, cfg.dtype)
 
-    # one common warm-up (clocks, caches, allocator) before any timed run
+    # one common warm-up (clocks, caches, allocator) before any timed run: at
+    # least 20 steps and one second, since the GPU reaches its steady clock only
+    # after some 100 ms of load (a first timed run right after 20 steps measured
+    # 8% slower than the next ones)
     log("warm-up")
+    t_warm = time.perf_counter()
     time_layer(moe, torch, shape, inp, 1, max(args.warmup, 20))
+    while time.perf_counter() - t_warm < 1.0:
+        time_layer(moe, torch, shape, inp, 1, 50)
     log(f"layer N={N}")
     main_run = time_layer(moe, torch, shape, inp, args.steps, args.warmup)
     log(f"layer N=1 (reference)")

@@ -682,9 +682,9 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     if (st != MOE_OK) return st;
     first = false;
     // permute backward: grad_hidden[t] = sum_j grad_x[dst_row[t*k+j]]
-    he = launch_combine(s, t0, t1, yg0, dst_row, nullptr, grad_hidden, s0);
-    if (he == hipSuccess && rows1 > 0)
-      he = launch_combine(s, u0, u1, yg1, dst_row, nullptr, grad_hidden, s0);
+    he = rows1 > 0 ? launch_combine_pair(s, t0, u0, u1, yg0, yg1, dst_row, nullptr, grad_hidden,
+                                         s0)
+                   : launch_combine(s, t0, t1, yg0, dst_row, nullptr, grad_hidden, s0);
     if (he != hipSuccess) return MOE_ERR_HIP;
   }
   if (first) {
@@ -761,15 +761,14 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
 
   if (schedule == MOE_SCHEDULE_PAIR_FUSED) {
     // Pair (c, c+1): one gate_up launch over the pair's rows (gathering them
-    // from hidden_states), one down launch, both combines, all on s0.  Every expert's weights are
-    // streamed once per pair.  (Running the second chunk's permute and combine
-    // on s1 measured slower: the stream joins cost more than overlapping two
-    // memory-bound kernels gains.)
+    // from hidden_states), one down launch, one combine launch for both
+    // chunks, all on s0.  Every expert's weights are streamed once per pair.
+    // (Running the second chunk's steps on s1 measured slower: the stream
+    // joins cost more than overlapping two memory-bound kernels gains.)
     for (int c = 0; c < s.N; c += 2) {
       int t0, t1, u0, u1;
       const int64_t rows0 = chunk_rows(c, &t0, &t1), rows1 = chunk_rows(c + 1, &u0, &u1);
       if (rows0 + rows1 == 0) continue;  // empty tail pair
-      hipStream_t st1 = s0;
       void* xy0 = w + p.slot[0];
       void* xy1 = p.nslots > 1 ? w + p.slot[1] : nullptr;
       const int32_t* off0 = offsets + (size_t)c * (s.E + 1);
@@ -797,9 +796,9 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
       dn.c_split = true;
       st = down(s, dn, w_down, s0);
       if (st != MOE_OK) return st;
-      he = launch_combine(s, t0, t1, xy0, dst_row, top_k_weights, out, s0);
-      if (he == hipSuccess && rows1 > 0)
-        he = launch_combine(s, u0, u1, xy1, dst_row, top_k_weights, out, st1);
+      he = rows1 > 0 ? launch_combine_pair(s, t0, u0, u1, xy0, xy1, dst_row, top_k_weights,
+                                           out, s0)
+                     : launch_combine(s, t0, t1, xy0, dst_row, top_k_weights, out, s0);
       if (he != hipSuccess) return MOE_ERR_HIP;
     }
   } else {

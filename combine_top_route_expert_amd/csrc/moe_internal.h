@@ -50,6 +50,10 @@ hipError_t launch_permute(const Shape& s, int t0, int t1, const void* hidden,
 // w may be null: unit weights (the permute backward, a gather-sum over k rows).
 hipError_t launch_combine(const Shape& s, int t0, int t1, const void* y,
                           const int32_t* dst_row, const float* w, void* out, hipStream_t st);
+// Both chunks of a pair in one launch: tokens [t0, t_mid) read y0, [t_mid, t1) y1.
+hipError_t launch_combine_pair(const Shape& s, int t0, int t_mid, int t1, const void* y0,
+                               const void* y1, const int32_t* dst_row, const float* w,
+                               void* out, hipStream_t st);
 
 // ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----------------------------
 // One grouped GEMM over the rows of one chunk, or of the two chunks of a pair.

@@ -76,15 +76,19 @@ __device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
 }
 
 // One wave per token; each lane holds kVecPerLane 16-byte vectors of the row.
+// Tokens [t0, t_mid) read their rows from y0, tokens [t_mid, t1) from y1 (a
+// chunk pair whose expert outputs sit in two slots; row indices are
+// chunk-local).
 template <bool kBf16>
 __global__ void __launch_bounds__(64 * kWavesPerBlock)
-combine_rows(const u32x4* __restrict__ y, const int32_t* __restrict__ dst_row,
-             const float* __restrict__ w, u32x4* __restrict__ out, int t0, int t1, int k,
-             int nvec) {
+combine_rows(const u32x4* __restrict__ y0, const u32x4* __restrict__ y1, int t_mid,
+             const int32_t* __restrict__ dst_row, const float* __restrict__ w,
+             u32x4* __restrict__ out, int t0, int t1, int k, int nvec) {
   constexpr int kEl = kBf16 ? 8 : 4;  // elements per 16-byte vector
   const int lane = threadIdx.x & 63;
   const int t = t0 + blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= t1) return;
+  const u32x4* __restrict__ y = t < t_mid ? y0 : y1;  // wave-uniform
   // the token's k rows and weights, one slot per lane, fetched in one round trip
   const int my_row = lane < k ? dst_row[(size_t)t * k + lane] : -1;
   const float my_w = lane < k ? (w ? w[(size_t)t * k + lane] : 1.0f) : 0.0f;
@@ -238,18 +242,26 @@ hipError_t launch_permute(const Shape& s, int t0, int t1, const void* hidden,
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Shape& s, int t0, int t1, const void* y,
-                          const int32_t* dst_row, const float* w, void* out, hipStream_t st) {
+hipError_t launch_combine_pair(const Shape& s, int t0, int t_mid, int t1, const void* y0,
+                               const void* y1, const int32_t* dst_row, const float* w,
+                               void* out, hipStream_t st) {
   if (t1 <= t0) return hipSuccess;
   const int nvec = (int)((int64_t)s.H * s.elem / 16);
   const unsigned blocks = (unsigned)((t1 - t0 + kWavesPerBlock - 1) / kWavesPerBlock);
   if (s.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_rows<true>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
-                       (const u32x4*)y, dst_row, w, (u32x4*)out, t0, t1, s.k, nvec);
+                       (const u32x4*)y0, (const u32x4*)y1, t_mid, dst_row, w, (u32x4*)out, t0,
+                       t1, s.k, nvec);
   else
     hipLaunchKernelGGL(combine_rows<false>, dim3(blocks), dim3(64 * kWavesPerBlock), 0, st,
-                       (const u32x4*)y, dst_row, w, (u32x4*)out, t0, t1, s.k, nvec);
+                       (const u32x4*)y0, (const u32x4*)y1, t_mid, dst_row, w, (u32x4*)out, t0,
+                       t1, s.k, nvec);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const Shape& s, int t0, int t1, const void* y,
+                          const int32_t* dst_row, const float* w, void* out, hipStream_t st) {
+  return launch_combine_pair(s, t0, t1, t1, y, y, dst_row, w, out, st);
 }
 
 }  // namespace moe
