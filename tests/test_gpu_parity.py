@@ -104,6 +104,10 @@ def test_route_meta_bit_exact(name, N, G):
     (1, 1, 8, 1, 1, 0.0),
     (2500, 8, 256, 16, 2, 1.0),  # every id dropped
     (0, 8, 256, 16, 4, 0.0),     # no tokens
+    (20000, 8, 64, 4, 2, 0.05),   # chunks of 80000 assignments (several per segment plan)
+    (300, 64, 1024, 16, 3, 0.02),  # largest E with dropped ids and three chunks
+    (5000, 8, 512, 8, 2, 0.03),
+    (16384, 8, 96, 3, 2, 0.01),    # E not a power of two, 65536 assignments per chunk
 ])
 def test_route_meta_edge_cases(T, k, E, G, N, bad):
     rng = np.random.default_rng(T + k + E)
