@@ -13,10 +13,11 @@
 //     straddle a chunk).  Lanes with equal expert id find each other with one
 //     ballot per id bit; the lowest such lane adds the group's popcount to the
 //     wave's LDS counter.  Writes seg_counts[seg][E] and the dropped-id count.
-//  2. meta_scan : one workgroup.  Per chunk and expert, an exclusive prefix over
-//     the chunk's segments (in place), then a block-wide exclusive scan over
-//     experts gives offsets; seg_counts becomes each segment's first row per
-//     expert.  Also counts, group splits, the -1 tail of src_row and dev_error.
+//  2. meta_scan : one workgroup per chunk.  Per expert, an exclusive prefix
+//     over the chunk's segments (in place), then a block-wide exclusive scan
+//     over experts gives offsets; seg_counts becomes each segment's first row
+//     per expert.  Also counts, group splits, the -1 tail of src_row, and (in
+//     workgroup 0) dev_error.
 //  3. meta_rank : one wave per segment again.  rank = popcount(peers below me)
 //     plus the segment's running base per expert gives dst_row[f] and
 //     src_row[chunk_start + row] = f.  Lanes are walked in ascending f, so the
@@ -145,55 +146,71 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds_waves) {
 __global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
   __shared__ int stage[kScanStage];
   __shared__ int lds_waves[48];
-  __shared__ int off_lds[1025];
-  const int e = threadIdx.x;
+  __shared__ int off_lds[kMaxExperts + 1];
+  const int c = blockIdx.x;  // one workgroup per chunk
+  // P consecutive lanes per expert (P a power of two, P * E <= 1024) share the
+  // prefix over the chunk's segments: each sums a contiguous run of segments,
+  // the P partial sums are scanned with lane shuffles, then each lane writes
+  // its segments' running prefix
+  int P = 64;
+  while (P > 1 && P * a.E > (int)blockDim.x) P >>= 1;
+  const int e = threadIdx.x / P, part = threadIdx.x % P;
   const bool has_e = e < a.E;
-  for (int c = 0; c < a.N; ++c) {
-    const size_t seg0 = (size_t)c * a.spc;
-    const int n_stage = a.spc * a.E;  // <= kScanStage by the plan
-    int32_t* blk = a.seg_counts + seg0 * a.E;
-    for (int i = threadIdx.x; i < n_stage; i += blockDim.x) stage[i] = blk[i];
-    __syncthreads();
-    int run = 0;
-    if (has_e) {
-      for (int j = 0; j < a.spc; ++j) {
-        const int v = stage[j * a.E + e];
-        stage[j * a.E + e] = run;
-        run += v;
-      }
-    }
-    int total;
-    int off = block_exclusive_scan(has_e ? run : 0, &total, lds_waves);
-    if (has_e) {
-      a.counts[(size_t)c * a.E + e] = run;
-      a.offsets[(size_t)c * (a.E + 1) + e] = off;
-      off_lds[e] = off;
-    }
-    if (e == 0) {
-      a.offsets[(size_t)c * (a.E + 1) + a.E] = total;
-      off_lds[a.E] = total;
-    }
-    __syncthreads();
-    // segment bases: chunk offset + prefix over the chunk's earlier segments
-    for (int i = threadIdx.x; i < n_stage; i += blockDim.x) blk[i] = stage[i] + off_lds[i % a.E];
-    const int per = a.E / a.G;
-    for (int g = threadIdx.x; g < a.G; g += blockDim.x)
-      a.splits[(size_t)c * a.G + g] = off_lds[(g + 1) * per] - off_lds[g * per];
-    // rows past the chunk's valid rows hold no assignment
-    long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
-    if (t0 > a.T) t0 = a.T;
-    if (t1 > a.T) t1 = a.T;
-    const long long f0 = t0 * a.k, ac = (t1 - t0) * a.k;
-    for (long long r = total + threadIdx.x; r < ac; r += blockDim.x) a.src_row[f0 + r] = -1;
-    __syncthreads();
+  const size_t seg0 = (size_t)c * a.spc;
+  const int n_stage = a.spc * a.E;  // <= kScanStage by the plan
+  int32_t* blk = a.seg_counts + seg0 * a.E;
+  for (int i = threadIdx.x; i < n_stage; i += blockDim.x) stage[i] = blk[i];
+  __syncthreads();
+  const int len = (a.spc + P - 1) / P;
+  const int j0 = part * len < a.spc ? part * len : a.spc;
+  const int j1 = j0 + len < a.spc ? j0 + len : a.spc;
+  int local = 0;
+  if (has_e)
+    for (int j = j0; j < j1; ++j) local += stage[j * a.E + e];
+  int incl = local;
+  for (int d = 1; d < P; d <<= 1) {
+    const int n = __shfl_up(incl, d, P);
+    if (part >= d) incl += n;
   }
-  if (a.dev_error) {
+  const int count_e = __shfl(incl, P - 1, P);
+  int run = incl - local;
+  if (has_e)
+    for (int j = j0; j < j1; ++j) {
+      const int v = stage[j * a.E + e];
+      stage[j * a.E + e] = run;
+      run += v;
+    }
+  const bool lead = has_e && part == 0;
+  int total;
+  const int off = block_exclusive_scan(lead ? count_e : 0, &total, lds_waves);
+  if (lead) {
+    a.counts[(size_t)c * a.E + e] = count_e;
+    a.offsets[(size_t)c * (a.E + 1) + e] = off;
+    off_lds[e] = off;
+  }
+  if (threadIdx.x == 0) {
+    a.offsets[(size_t)c * (a.E + 1) + a.E] = total;
+    off_lds[a.E] = total;
+  }
+  __syncthreads();
+  // segment bases: chunk offset + prefix over the chunk's earlier segments
+  for (int i = threadIdx.x; i < n_stage; i += blockDim.x) blk[i] = stage[i] + off_lds[i % a.E];
+  const int per = a.E / a.G;
+  for (int g = threadIdx.x; g < a.G; g += blockDim.x)
+    a.splits[(size_t)c * a.G + g] = off_lds[(g + 1) * per] - off_lds[g * per];
+  // rows past the chunk's valid rows hold no assignment
+  long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
+  if (t0 > a.T) t0 = a.T;
+  if (t1 > a.T) t1 = a.T;
+  const long long f0 = t0 * a.k, ac = (t1 - t0) * a.k;
+  for (long long r = total + threadIdx.x; r < ac; r += blockDim.x) a.src_row[f0 + r] = -1;
+  if (a.dev_error && c == 0) {
     int s = 0;
     const long long nseg = (long long)a.N * a.spc;
     for (long long i = threadIdx.x; i < nseg; i += blockDim.x) s += a.seg_invalid[i];
-    int total;
-    (void)block_exclusive_scan(s, &total, lds_waves);
-    if (threadIdx.x == 0) *a.dev_error = total;
+    int dropped;
+    (void)block_exclusive_scan(s, &dropped, lds_waves);
+    if (threadIdx.x == 0) *a.dev_error = dropped;
   }
 }
 
@@ -282,7 +299,7 @@ hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts
   a.id_bits = bits_for(s.E);
   const size_t lds = (size_t)s.E * sizeof(int);
   hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
-  hipLaunchKernelGGL(meta_scan, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(meta_scan, dim3((unsigned)s.N), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
   return hipGetLastError();
 }
