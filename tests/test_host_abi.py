@@ -157,6 +157,16 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                 fake, None) == 1
     assert _raw("moe_expert_ffn_pair", sp, 2, fake, fake, fake, fake, fake, fake, fake, fake,
                 None) == 1
+    # gate/up with rows gathered from hidden_states: null src_row, misaligned
+    # hidden_states or src_row, bad chunk
+    assert _raw("moe_expert_gate_up_gather_pair", sp, 0, fake, None, fake, fake, fake,
+                None) == 1
+    assert _raw("moe_expert_gate_up_gather_pair", sp, 0, fake + 2, fake, fake, fake, fake,
+                None) == 1
+    assert _raw("moe_expert_gate_up_gather_pair", sp, 0, fake, fake + 2, fake, fake, fake,
+                None) == 1
+    assert _raw("moe_expert_gate_up_gather_pair", sp, 2, fake, fake, fake, fake, fake,
+                None) == 1
     # backward: too-small workspace, misaligned grad_out, null weight gradients
     need_b = moe.moe_backward_workspace_size(shape)
     args = [fake] * 10  # hidden .. grad_w_down
@@ -191,6 +201,8 @@ def test_empty_chunk_calls_are_noops():
     assert _raw("moe_permute_backward", sp, 3, None, None, None, None) == 0
     # a pair whose chunks are both empty; none of its pointers is needed
     assert _raw("moe_expert_ffn_pair", sp, 3, None, None, None, None, None, None, None, None,
+                None) == 0
+    assert _raw("moe_expert_gate_up_gather_pair", sp, 3, None, None, None, None, None,
                 None) == 0
 
 
