@@ -246,9 +246,8 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  *    gathers each row straight from hidden_states through src_row (the permute
  *    fused into the GEMM's row addressing: same rows, same bits, no x_perm
  *    buffer traffic), one down launch, one combine launch for both chunks, all
- *    on s0 (s1 is not
- *    used: on MI355X the joins that would let the second chunk's steps overlap
- *    on s1 cost more than the overlap gains).
+ *    on s0 (s1 is not used: on MI355X the joins that would let the second
+ *    chunk's steps overlap on s1 cost more than the overlap gains).
  *  MOE_SCHEDULE_PER_CHUNK: chunk c runs permute -> gate_up -> down -> combine on
  *    stream s[c % 2] in slot c % 2, so the two chunks of a pair overlap as whole
  *    pipelines; every chunk streams the expert weights again.
