@@ -430,9 +430,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
   const int KT = (rows + BK - 1) / BK;
+  const int KF = rows / BK;  // stages whose BK rows all exist
   if (KT > 0) issue(0, 0);
   const int g = lane >> 4;
-  for (int kt = 0; kt < KT; ++kt) {
+  // one stage; kTail: the last, partial stage (K rows past the expert's block
+  // are zeroed in the A fragments).  Full stages run a body without branches.
+  auto stage = [&](int kt, auto tail_const) {
+    constexpr bool kTail = decltype(tail_const)::value;
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __builtin_amdgcn_s_barrier();
     if (kt + 1 < KT) issue(kt + 1, (kt + 1) & 1);
@@ -441,20 +445,24 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
     const int kvalid = rows - kt * BK;  // K rows of this stage that exist
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      if (16 * kk >= kvalid) break;
+      if constexpr (kTail) {
+        if (16 * kk >= kvalid) break;
+      }
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int cb = wm * WM + i * 32;
         af[i] = tr_frag(sa, GA::tr_offset(lane, cb, kk, 0), GA::tr_offset(lane, cb, kk, 1));
       }
-      if (16 * kk + 16 > kvalid) {
-        // element j of half h is K row 16kk + 8(g/2) + 4h + j: zero rows past the block
+      if constexpr (kTail) {
+        if (16 * kk + 16 > kvalid) {
+          // element j of half h is K row 16kk + 8(g/2) + 4h + j: zero rows past the block
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int x = 0; x < 8; ++x)
-            if (16 * kk + 8 * (g >> 1) + x >= kvalid) af[i][x] = (__bf16)0.0f;
+            for (int x = 0; x < 8; ++x)
+              if (16 * kk + 8 * (g >> 1) + x >= kvalid) af[i][x] = (__bf16)0.0f;
+        }
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -468,7 +476,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  }
+  };
+  for (int kt = 0; kt < KF; ++kt) stage(kt, std::false_type{});
+  if (KF < KT) stage(KF, std::true_type{});
 
   float* Ce = a.C + (int64_t)e * a.M * a.N;
   const int rbase = wm * WM + 4 * (lane >> 5);
