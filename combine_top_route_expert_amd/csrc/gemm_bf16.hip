@@ -96,6 +96,14 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// SwiGLU of one gate/up pair: silu(g) * u = g / (1 + e^-g) * u, with the
+// hardware base-2 exponential (__expf) and reciprocal (v_rcp_f32): a few ulp
+// of fp32, far below the bf16 rounding of the result.  e^-g overflowing to
+// infinity gives g * 0 = 0, the limit.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // LDS layout of one stage: BM rows of A then BN rows of B, each row BK bf16
 // (ROW_BYTES) holding CH 16-byte chunks; chunk c of row r sits at slot
 // c ^ swz(r).  A 16-lane phase of a 16-byte fragment read covers 16
@@ -231,7 +239,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
         for (int j = 0; j < FN / 2; ++j) {
           const int col = nt * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
           const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
-          crow[col] = to_bf16_bits(g / (1.0f + expf(-g)) * u);
+          crow[col] = to_bf16_bits(swiglu(g, u));
         }
         if (a.gu) {  // the backward's saved pre-activations
           uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
@@ -250,6 +258,58 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc
         }
       }
     }
+}
+
+// Epilogue through LDS: every wave writes its blocks (after SwiGLU for gate_up)
+// as bf16 into a row-major C tile in the freed stage buffers, then the
+// workgroup stores the tile 16 bytes per lane, one row segment at a time.
+// (Storing each lane's 2-byte elements straight from the MFMA layout took one
+// guarded global store per element.)  Chunk ch (8 elements) of tile row r
+// sits at chunk ch ^ 4((r/4) mod 2), so that the two rows a 2-byte LDS write
+// covers (r and r + 4) fall in different banks.  Same values, same bits.
+template <bool kGateUp, int FM, int FN, int BM, int BN, int WM, int WN, int NT>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
+                                               const TileRows& tr, int nt, int wm, int wn,
+                                               int lane, char* smem) {
+  constexpr int CT = kGateUp ? BN / 2 : BN;  // tile columns of C
+  constexpr int CPR = CT / 8;                // 16-byte chunks per tile row
+  static_assert(CPR >= 8, "chunk swizzle needs 8 chunks per row");
+  auto lds_at = [](int r, int c) {
+    return r * (CT * 2) + ((((c >> 3) ^ (((r >> 2) & 1) << 2))) << 4) + (c & 7) * 2;
+  };
+  const int rbase = wm * WM + 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    if (wm * WM + i * 32 >= tr.rows) break;  // blocks past the tile's rows: never stored
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+      if constexpr (kGateUp) {
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int c = wn * (WN / 2) + j * 32 + (lane & 31);
+          const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
+          *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(swiglu(g, u));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int c = wn * WN + j * 32 + (lane & 31);
+          *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(acc[i][j][q]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
+  const int col0 = nt * CT;
+  for (int ch = threadIdx.x; ch < BM * CPR; ch += NT) {
+    const int r = ch / CPR, c = (ch % CPR) * 8;
+    if (r >= tr.rows || col0 + c >= a.ncols) continue;
+    const uint4 v = *(const uint4*)(smem + lds_at(r, c));
+    uint16_t* crow = (uint16_t*)row_ptr(cbase, a.c_split, tr, tr.v0 + r, a.ncols);
+    *(uint4*)(crow + col0 + c) = v;
+  }
 }
 
 // The K loop of one wave.  F (<= FM) 32-row blocks of the wave's band take
@@ -351,7 +411,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       MOE_K_LOOP(0);
   }
 #undef MOE_K_LOOP
-  store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
+  if (a.gu) {
+    // the backward's recompute also saves g and u: per-element stores
+    store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
+    return;
+  }
+  static_assert(BM * (kGateUp ? BN / 2 : BN) * 2 <= STAGES * Loader::STAGE_BYTES,
+                "C tile fits the stage buffers");
+  __syncthreads();  // every wave is done with the stage buffers
+  store_tile_lds<kGateUp, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, wm, wn, lane, smem);
 }
 
 // Tile instances.  Both use the same MFMA instruction and the same order of
