@@ -323,29 +323,36 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
       }
     return;
   }
+  // plain: the C tile goes through the freed stage buffers as row-major bf16
+  // (chunk ch of row r at ch ^ 4((r/4) mod 2), so the rows r and r + 4 of one
+  // 2-byte write fall in different banks), then out as 16-byte row segments
+  static_assert(BM * BN * 2 <= 2 * STAGE && BN / 8 >= 8, "C tile in the stage buffers");
+  constexpr int CPR = BN / 8;
+  auto lds_at = [](int r, int c) {
+    return r * (BN * 2) + (((c >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (c & 7) * 2;
+  };
+  __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    if (wm * WM + i * 32 >= tr.rows) break;  // blocks past the tile's rows: never stored
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-      if (row >= tr.rows) continue;
-      const int v = tr.v0 + row;
-      {
-        uint16_t* cr;
-        if (a.c_split) {
-          int part;
-          const int r = tr.split_row(v, &part);
-          cr = a.C[part] + (int64_t)r * a.N;
-        } else {
-          cr = a.C[0] + (int64_t)tr.joint_row(v) * a.N;
-        }
+      const int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
-          if (col < a.N) cr[col] = to_bf16_bits(acc[i][j][q]);
-        }
+      for (int j = 0; j < FN; ++j) {
+        const int c = wn * WN + j * 32 + (lane & 31);
+        *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(acc[i][j][q]);
       }
     }
+  }
+  __syncthreads();
+  const SideU c_u = uniform_side(Side{{a.C[0], a.C[1]}, a.c_split, a.N});
+  for (int ch = threadIdx.x; ch < BM * CPR; ch += blockDim.x) {
+    const int r = ch / CPR, c = (ch % CPR) * 8;
+    if (r >= tr.rows || nt * BN + c >= a.N) continue;
+    const uint4 v = *(const uint4*)(smem + lds_at(r, c));
+    *(uint4*)side_addr(c_u, tr, tr.v0 + r, nt * BN + c) = v;
+  }
 }
 
 // ---- wgrad ------------------------------------------------------------------------
