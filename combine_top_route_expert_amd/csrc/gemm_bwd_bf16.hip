@@ -487,57 +487,45 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
   for (int kt = 0; kt < KF; ++kt) stage(kt, std::false_type{});
   if (KF < KT) stage(KF, std::true_type{});
 
+  // The fp32 C tile goes through the freed stage buffers in two passes of
+  // WM rows (the two wave rows), row-major, and out as 16-byte row segments:
+  // one global store (and, when accumulating, one load) per 4 elements
+  // instead of per element.
+  static_assert(WAVES_M == 2 && WM * BN * 4 <= 2 * STAGE, "half C tile in the stage buffers");
+  constexpr int CPR = BN / 4;  // 16-byte chunks per row
   float* Ce = a.C + (int64_t)e * a.M * a.N;
-  const int rbase = wm * WM + 4 * (lane >> 5);
-  if (a.accumulate) {
-    // per 32-row block: all loads of the previous sums first, then the stores
+  float* cl = (float*)smem;
+  const int rl = 4 * (lane >> 5);  // row of q = 0 within a 32-row block
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float old[16][FN];
+  for (int h = 0; h < WAVES_M; ++h) {
+    __syncthreads();  // the stage buffers (or the previous pass) are free
+    if (wm == h) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        int m = mt * BM + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-        m = m < a.M ? m : a.M - 1;
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          int n = nt * BN + wn * WN + j * 32 + (lane & 31);
-          n = n < a.N ? n : a.N - 1;
-          old[q][j] = Ce[(int64_t)m * a.N + n];
+        for (int q = 0; q < 16; ++q) {
+          const int r = rl + i * 32 + 8 * (q >> 2) + (q & 3);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) cl[r * BN + wn * WN + j * 32 + (lane & 31)] = acc[i][j][q];
         }
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          old[q][j] += acc[i][j][q];
-          pin(old[q][j]);
-        }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = mt * BM + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-        if (m >= a.M) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = nt * BN + wn * WN + j * 32 + (lane & 31);
-          if (n < a.N) Ce[(int64_t)m * a.N + n] = old[q][j];
-        }
-      }
     }
-    return;
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < WM * CPR; ch += blockDim.x) {
+      const int r = ch / CPR, c = (ch % CPR) * 4;
+      const int m = mt * BM + h * WM + r, n = nt * BN + c;
+      if (m >= a.M || n >= a.N) continue;
+      float4 v = *(const float4*)(cl + r * BN + c);
+      float4* dst = (float4*)(Ce + (int64_t)m * a.N + n);
+      if (a.accumulate) {
+        const float4 old = *dst;
+        v.x = old.x + v.x;
+        v.y = old.y + v.y;
+        v.z = old.z + v.z;
+        v.w = old.w + v.w;
+      }
+      *dst = v;
+    }
   }
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int m = mt * BM + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-      if (m >= a.M) continue;
-      float* cr = Ce + (int64_t)m * a.N;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int n = nt * BN + wn * WN + j * 32 + (lane & 31);
-        if (n < a.N) cr[n] = acc[i][j][q];
-      }
-    }
 }
 
 }  // namespace
