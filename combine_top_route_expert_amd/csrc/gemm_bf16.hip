@@ -41,6 +41,12 @@
 // workgroups exit.  Rows past an expert's block are loaded from a clamped row
 // (A blocks wholly past it are not loaded at all) and never stored.
 //
+// Small tiles: an m-tile of at most 32 or 64 rows (a small expert's only
+// tile) has little MFMA work and is bound by streaming its weight panel, so it
+// runs a K loop with a compact stage layout (its rows of A, then B) and three
+// stages, two in flight (k_loop_small): 41 -> 33 us per gate/up tile of at
+// most 32 rows on the Zipf workload.
+//
 // What bounds it (measured with per-workgroup timestamps): the MFMA loop alone
 // (no global loads) runs at ~94% of the matrix peak at the clock it gets, and
 // adding the LDS fragment reads costs nothing.  With the operand streaming on
@@ -91,6 +97,8 @@ __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* const (&base)
   }
   return base[0] + (int64_t)tr.joint_row(v) * ld;
 }
+
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
@@ -179,6 +187,28 @@ struct TileLoader {
       }
       b_src[t] = (const char*)(Be + (int64_t)brow * a.K + chunk * 8);
     }
+  }
+
+  // Compact stage of a tile with at most SROWS rows: those rows of A (the
+  // first blocks, which only the first waves hold) then the BN rows of B.
+  template <int SROWS>
+  static constexpr int small_a() { return SROWS * G::ROW_BYTES; }
+  template <int SROWS>
+  static constexpr int small_stage() { return small_a<SROWS>() + BN * G::ROW_BYTES; }
+  template <int SROWS>
+  __device__ __forceinline__ void issue_small(char* smem, int kt, int buf) const {
+    char* base = smem + buf * small_stage<SROWS>();
+    const int64_t koff = (int64_t)kt * G::ROW_BYTES;
+#pragma unroll
+    for (int t = 0; t < LA; ++t)
+      if (t < live_a)  // blocks past the tile's (at most SROWS) rows are not live
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff),
+                                         (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < LB; ++t)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(b_src[t] + koff),
+          (lds_void*)(base + small_a<SROWS>() + (wave * LB + t) * 1024), 16, 0, 0);
   }
 
   // Loads one stage.  A blocks of 1 KB that lie wholly past the tile's rows are
@@ -353,6 +383,50 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
   }
 }
 
+// The K loop of a tile with at most SROWS (32 or 64) rows: such a tile (a
+// small expert's only m-tile) is bound by streaming its B panel rather than by
+// MFMAs, so it uses the compact stage layout and SSTAGES stages (SSTAGES - 1 in
+// flight) to keep more weight bytes in flight.  kMfma: the wave holds the
+// tile's rows (wave row 0, F = SROWS / 32 blocks); the other waves only load
+// and join the barriers.
+template <bool kMfma, int SROWS, int SSTAGES, int FM, int FN, int WN, int BK, class Loader>
+__device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
+                                             int KT, int per_stage, int lane, int wn) {
+  using G = StageGeom<BK>;
+  constexpr int F = SROWS / 32;
+  constexpr int STAGE = Loader::template small_stage<SROWS>();
+#pragma unroll
+  for (int s = 0; s < SSTAGES - 1; ++s)
+    if (s < KT) ld.template issue_small<SROWS>(smem, s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int newer = KT - 1 - kt < SSTAGES - 2 ? KT - 1 - kt : SSTAGES - 2;
+    wait_loads(newer * per_stage);
+    __builtin_amdgcn_s_barrier();
+    if (kt + SSTAGES - 1 < KT)
+      ld.template issue_small<SROWS>(smem, kt + SSTAGES - 1, (kt + SSTAGES - 1) % SSTAGES);
+    if constexpr (kMfma) {
+      const char* sa = smem + (kt % SSTAGES) * STAGE;
+      const char* sb = sa + Loader::template small_a<SROWS>();
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int fo = G::frag_offset(lane, kk);
+        bf16x8 af[F], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < F; ++i) af[i] = *(const bf16x8*)(sa + i * 32 * G::ROW_BYTES + fo);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+}
+
 template <bool kGateUp, int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(GemmArgs a) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -363,7 +437,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   static_assert(!kGateUp || WN % 64 == 0, "gate/up halves");
   static_assert(STAGES >= 2, "pipeline depth");
   static_assert((STAGES - 2) * (Loader::LA + Loader::LB) <= 24, "wait_loads range");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * Loader::STAGE_BYTES];
+  constexpr int kSmemBytes =
+      cmax(STAGES * Loader::STAGE_BYTES,
+           FM >= 4 ? cmax(3 * Loader::template small_stage<32>(),
+                          3 * Loader::template small_stage<64>())
+                   : 0);
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -386,6 +465,20 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
   const int KT = a.K / BK;
+  // tiles of at most 32 or 64 rows: three compact stages (a fourth stage for
+  // the 32-row tiles, in 16 KB more LDS, measured no faster)
+  constexpr bool kSmallPath = FM >= 4 && WAVES_M == 2;
+  if (kSmallPath && tr.rows <= 32) {
+    if (wm == 0)
+      k_loop_small<true, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+    else
+      k_loop_small<false, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+  } else if (kSmallPath && tr.rows <= 64) {
+    if (wm == 0)
+      k_loop_small<true, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+    else
+      k_loop_small<false, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+  } else {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) ld.issue(smem, s, s);
@@ -411,6 +504,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       MOE_K_LOOP(0);
   }
 #undef MOE_K_LOOP
+  }
   if (a.gu) {
     // the backward's recompute also saves g and u: per-element stores
     store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
