@@ -323,7 +323,14 @@ __device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* m
   if (ml >= C1) {
     j = ns - R + (ml - C1);
   } else {
-    const int lb = (int)((long long)ml * nl / C1), la = (int)((long long)(ml + 1) * nl / C1);
+    int lb, la;  // large m-tiles before positions ml and ml + 1
+    if (C1 < 65536) {  // nl <= C1: the products fit 32 bits
+      lb = (int)((unsigned)ml * (unsigned)nl / (unsigned)C1);
+      la = (int)((unsigned)(ml + 1) * (unsigned)nl / (unsigned)C1);
+    } else {
+      lb = (int)((long long)ml * nl / C1);
+      la = (int)((long long)(ml + 1) * nl / C1);
+    }
     if (la > lb) {
       *mt = x * per + lb;
       return true;
