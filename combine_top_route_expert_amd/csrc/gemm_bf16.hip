@@ -250,95 +250,68 @@ __device__ __forceinline__ void wait_loads(int n) {
 #undef MOE_WAIT_CASE
 }
 
-// Epilogue for one wave's FM x FN blocks.  MFMA 32x32 output: lane l holds
-// column l % 32 of rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of each block.
-template <bool kGateUp, int FM, int FN, int BN, int WM, int WN>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
-                                           const TileRows& tr, int nt, int wm, int wn, int lane) {
-  const int rbase = wm * WM + 4 * (lane >> 5);
-  const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-      if (row >= tr.rows) continue;
-      uint16_t* crow = (uint16_t*)row_ptr(cbase, a.c_split, tr, tr.v0 + row, a.ncols);
-      if constexpr (kGateUp) {
-#pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int col = nt * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
-          const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
-          crow[col] = to_bf16_bits(swiglu(g, u));
-        }
-        if (a.gu) {  // the backward's saved pre-activations
-          uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
-#pragma unroll
-          for (int j = 0; j < FN / 2; ++j) {
-            const int col = nt * (BN / 2) + wn * (WN / 2) + j * 32 + (lane & 31);
-            gr[col] = to_bf16_bits(acc[i][j][q]);
-            gr[a.I + col] = to_bf16_bits(acc[i][j + FN / 2][q]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
-          if (col < a.ncols) crow[col] = to_bf16_bits(acc[i][j][q]);
-        }
-      }
-    }
-}
-
-// Epilogue through LDS: every wave writes its blocks (after SwiGLU for gate_up)
-// as bf16 into a row-major C tile in the freed stage buffers, then the
-// workgroup stores the tile 16 bytes per lane, one row segment at a time.
-// (Storing each lane's 2-byte elements straight from the MFMA layout took one
-// guarded global store per element.)  Chunk ch (8 elements) of tile row r
-// sits at chunk ch ^ 4((r/4) mod 2), so that the two rows a 2-byte LDS write
-// covers (r and r + 4) fall in different banks.  Same values, same bits.
-template <bool kGateUp, int FM, int FN, int BM, int BN, int WM, int WN, int NT>
+// Epilogue through LDS.  MFMA 32x32 output: lane l holds column l % 32 of
+// rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of each block.  Every wave writes
+// its blocks (after SwiGLU for gate_up) as bf16 into a row-major C tile in the
+// freed stage buffers, then the workgroup stores the tile 16 bytes per lane,
+// one row segment at a time.  (Storing each lane's 2-byte elements straight
+// from the MFMA layout took one guarded global store per element.)  Chunk ch
+// (8 elements) of tile row r sits at chunk ch ^ 4((r/4) mod 2), so that the
+// two rows a 2-byte LDS write covers (r and r + 4) fall in different banks.
+// Same values, same bits.  PLANES = 3 (gate_up in the backward's recompute)
+// also saves g and u into the joint [rows][2I] copy: one plane per pass.
+template <bool kGateUp, int PLANES, int FM, int FN, int BM, int BN, int WM, int WN, int NT>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
                                                const TileRows& tr, int nt, int wm, int wn,
                                                int lane, char* smem) {
   constexpr int CT = kGateUp ? BN / 2 : BN;  // tile columns of C
   constexpr int CPR = CT / 8;                // 16-byte chunks per tile row
   static_assert(CPR >= 8, "chunk swizzle needs 8 chunks per row");
+  static_assert(PLANES == 1 || kGateUp, "g and u exist for gate_up only");
   auto lds_at = [](int r, int c) {
     return r * (CT * 2) + ((((c >> 3) ^ (((r >> 2) & 1) << 2))) << 4) + (c & 7) * 2;
   };
   const int rbase = wm * WM + 4 * (lane >> 5);
+  const int col0 = nt * CT;
+  const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    if (wm * WM + i * 32 >= tr.rows) break;  // blocks past the tile's rows: never stored
+  for (int plane = 0; plane < PLANES; ++plane) {
+    if (plane > 0) __syncthreads();  // the previous plane's reads are done
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-      if constexpr (kGateUp) {
+    for (int i = 0; i < FM; ++i) {
+      if (wm * WM + i * 32 >= tr.rows) break;  // blocks past the tile's rows: never stored
 #pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int c = wn * (WN / 2) + j * 32 + (lane & 31);
-          const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
-          *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(swiglu(g, u));
-        }
-      } else {
+      for (int q = 0; q < 16; ++q) {
+        const int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        if constexpr (kGateUp) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int c = wn * WN + j * 32 + (lane & 31);
-          *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(acc[i][j][q]);
+          for (int j = 0; j < FN / 2; ++j) {
+            const int c = wn * (WN / 2) + j * 32 + (lane & 31);
+            const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
+            const float v = plane == 0 ? swiglu(g, u) : plane == 1 ? g : u;
+            *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(v);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int c = wn * WN + j * 32 + (lane & 31);
+            *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(acc[i][j][q]);
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
-  const int col0 = nt * CT;
-  for (int ch = threadIdx.x; ch < BM * CPR; ch += NT) {
-    const int r = ch / CPR, c = (ch % CPR) * 8;
-    if (r >= tr.rows || col0 + c >= a.ncols) continue;
-    const uint4 v = *(const uint4*)(smem + lds_at(r, c));
-    uint16_t* crow = (uint16_t*)row_ptr(cbase, a.c_split, tr, tr.v0 + r, a.ncols);
-    *(uint4*)(crow + col0 + c) = v;
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < BM * CPR; ch += NT) {
+      const int r = ch / CPR, c = (ch % CPR) * 8;
+      if (r >= tr.rows || col0 + c >= a.ncols) continue;
+      const uint4 v = *(const uint4*)(smem + lds_at(r, c));
+      uint16_t* dst;
+      if (plane == 0)
+        dst = (uint16_t*)row_ptr(cbase, a.c_split, tr, tr.v0 + r, a.ncols);
+      else  // g (plane 1) or u (plane 2) of the joint [rows][2I] copy
+        dst = a.gu + (int64_t)tr.joint_row(tr.v0 + r) * (2 * a.I) + (plane - 1) * a.I;
+      *(uint4*)(dst + col0 + c) = v;
+    }
   }
 }
 
@@ -427,7 +400,8 @@ __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader
   }
 }
 
-template <bool kGateUp, int BM, int BN, int WAVES_M, int WAVES_N, int BK, int STAGES>
+template <bool kGateUp, bool kSaveGU, int BM, int BN, int WAVES_M, int WAVES_N, int BK,
+          int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(GemmArgs a) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -505,15 +479,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   }
 #undef MOE_K_LOOP
   }
-  if (a.gu) {
-    // the backward's recompute also saves g and u: per-element stores
-    store_tile<kGateUp, FM, FN, BN, WM, WN>(a, acc, tr, nt, wm, wn, lane);
-    return;
-  }
   static_assert(BM * (kGateUp ? BN / 2 : BN) * 2 <= STAGES * Loader::STAGE_BYTES,
                 "C tile fits the stage buffers");
   __syncthreads();  // every wave is done with the stage buffers
-  store_tile_lds<kGateUp, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, wm, wn, lane, smem);
+  store_tile_lds<kGateUp, kSaveGU ? 3 : 1, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, wm, wn,
+                                                                           lane, smem);
 }
 
 // Tile instances.  Both use the same MFMA instruction and the same order of
@@ -533,7 +503,7 @@ bool prefer_wide(int64_t rows_bound, int E, int K, int ncols) {
   return rows_bound >= 4096 && (avg >= 192 || K >= 4096 || ncols >= 4096);
 }
 
-template <bool kGateUp, int BM, int BN, int WM_, int WN_, int BK, int ST>
+template <bool kGateUp, bool kSaveGU, int BM, int BN, int WM_, int WN_, int BK, int ST>
 hipError_t launch_instance(GemmArgs a, const Shape& s, int64_t rows_bound, hipStream_t st) {
   constexpr int threads = 64 * WM_ * WN_;
   // gate_up tiles cover BN/2 intermediate columns (gate and up halves)
@@ -541,12 +511,12 @@ hipError_t launch_instance(GemmArgs a, const Shape& s, int64_t rows_bound, hipSt
   const int64_t grid = xcd_grid(m_tiles_bound(rows_bound, s.E, BM), a.n_tiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((grouped_gemm_bf16<kGateUp, BM, BN, WM_, WN_, BK, ST>), dim3((unsigned)grid),
-                     dim3(threads), 0, st, a);
+  hipLaunchKernelGGL((grouped_gemm_bf16<kGateUp, kSaveGU, BM, BN, WM_, WN_, BK, ST>),
+                     dim3((unsigned)grid), dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
-template <bool kGateUp>
+template <bool kGateUp, bool kSaveGU>
 hipError_t launch_kind(int inst, GemmArgs a, const Shape& s, int64_t rows_bound, hipStream_t st) {
   // a 256-column gate_up tile holds 128 intermediate columns
   const bool wide_ok = !kGateUp || s.I % 128 == 0;
@@ -555,8 +525,8 @@ hipError_t launch_kind(int inst, GemmArgs a, const Shape& s, int64_t rows_bound,
     inst = prefer_wide(rows_bound, s.E, a.K, ncols) ? kWide : kNarrow;
   }
   if (inst == kWide && wide_ok)
-    return launch_instance<kGateUp, 256, 256, 2, 4, 64, 2>(a, s, rows_bound, st);
-  return launch_instance<kGateUp, 64, 128, 2, 2, 64, 2>(a, s, rows_bound, st);
+    return launch_instance<kGateUp, kSaveGU, 256, 256, 2, 4, 64, 2>(a, s, rows_bound, st);
+  return launch_instance<kGateUp, kSaveGU, 64, 128, 2, 2, 64, 2>(a, s, rows_bound, st);
 }
 
 hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void* B,
@@ -584,12 +554,15 @@ hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void*
     a.K = s.H;
     a.ncols = s.I;
     a.b_expert_stride = (int64_t)2 * s.I * s.H;
-    return launch_kind<true>(inst, a, s, rows_bound, st);
+    // the backward's recompute also saves g and u (its own instance, so the
+    // forward kernel keeps its registers)
+    if (a.gu) return launch_kind<true, true>(inst, a, s, rows_bound, st);
+    return launch_kind<true, false>(inst, a, s, rows_bound, st);
   }
   a.K = s.I;
   a.ncols = s.H;
   a.b_expert_stride = (int64_t)s.H * s.I;
-  return launch_kind<false>(inst, a, s, rows_bound, st);
+  return launch_kind<false, false>(inst, a, s, rows_bound, st);
 }
 
 }  // namespace
