@@ -8,7 +8,9 @@
 // Both operands are K-contiguous ([rows][K] activations, [cols][K] weights).
 // One launch covers one chunk or both chunks of a pair (GroupedIO): an
 // expert's rows are its rows in the first chunk followed by its rows in the
-// second, so its weights are streamed once per launch.
+// second, so its weights are streamed once per launch.  gate_up may read its
+// rows straight from hidden_states through src_row (GroupedIO::gather): the
+// permute fused into the A loader's addresses.
 //
 // Pipeline: K advances BK (64) at a time.  Each stage of the A (rows) and B
 // (weight) tiles is copied global -> LDS by the direct-to-LDS load
@@ -41,6 +43,9 @@
 // workgroups exit.  Rows past an expert's block are loaded from a clamped row
 // (A blocks wholly past it are not loaded at all) and never stored.
 //
+// Epilogue: the accumulators go through the freed stage buffers as a
+// row-major bf16 tile and leave as 16-byte row segments (store_tile_lds).
+//
 // Small tiles: an m-tile of at most 32 or 64 rows (a small expert's only
 // tile) has little MFMA work and is bound by streaming its weight panel, so it
 // runs a K loop with a compact stage layout (its rows of A, then B) and three
@@ -54,9 +59,11 @@
 // 1.5-2.1 GHz) and a full 256 x 256 tile takes ~1.45x the cycles of its MFMAs.
 // Deeper pipelines (BK 32 with 4-5 stages, a third weight buffer),
 // register-staged loads, loads interleaved with the MFMAs, round-robin XCD
-// dealing and 4-wave 128 x 128 wave tiles all measured no faster.  What did
-// help (5-12% on the larger workloads): a K loop whose body holds no branch,
-// with the wave's count of live 32-row blocks chosen once before the loop.
+// dealing of all m-tiles and 4-wave 128 x 128 wave tiles all measured no
+// faster.  What did help: a K loop whose body holds no branch, with the wave's
+// count of live 32-row blocks chosen once before the loop (5-12% on the larger
+// workloads); the size-balanced, interleaved tile order (xcd_tile); the staged
+// epilogue; the compact small-tile loop.
 #include <algorithm>
 
 #include "moe_internal.h"
