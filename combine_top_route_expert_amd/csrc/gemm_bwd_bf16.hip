@@ -271,56 +271,62 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
   // epilogue: lane l holds column l % 32 of rows 8(q/4) + 4(l/32) + q%4 of each block
   const int rbase = wm * WM + 4 * (lane >> 5);
   if constexpr (kEpi == kDgradSwiglu) {
-    // per 8-row half block: all of its g/u loads first, then the arithmetic and
-    // the stores, so one wait covers the half block (a wait per row would also
-    // wait for every earlier store)
+    // g and u of the tile's rows go through the freed stage buffers, one wave
+    // row (WM tile rows) per pass: read and written back as 16-byte row
+    // segments, the gradients computed in place in LDS by the wave row that
+    // holds those rows.  Chunk ch of row r at ch ^ 4((r/4) mod 2), as in the
+    // forward epilogue.
+    static_assert(WAVES_M == 2 && 2 * WM * BN * 2 <= 2 * STAGE && BN / 8 >= 8,
+                  "g and u of one wave row in the stage buffers");
+    constexpr int CPR = BN / 8;  // 16-byte chunks per row
+    char* lg = smem;
+    char* lu = smem + WM * BN * 2;
+    auto at = [](int r, int c) {
+      return r * (BN * 2) + (((c >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (c & 7) * 2;
+    };
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int h = 0; h < WAVES_M; ++h) {
+      __syncthreads();  // the stage buffers (or the previous pass) are free
+      for (int ch = threadIdx.x; ch < WM * CPR; ch += blockDim.x) {
+        const int r = ch / CPR, c = (ch % CPR) * 8;
+        const int row = h * WM + r, col = nt * BN + c;
+        if (row >= tr.rows || col >= a.N) continue;
+        const uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
+        *(uint4*)(lg + at(r, c)) = *(const uint4*)(gr + col);
+        *(uint4*)(lu + at(r, c)) = *(const uint4*)(gr + a.I + col);
+      }
+      __syncthreads();
+      if (wm == h) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // rows q = 8h .. 8h+7 of the block
-        uint16_t gv[8][FN], uv[8][FN];
+        for (int i = 0; i < FM; ++i) {
+          if (h * WM + i * 32 >= tr.rows) break;  // rows past the tile: never stored
 #pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int q = 8 * h + qq;
-          const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-          const int rr = row < tr.rows ? row : tr.rows - 1;
-          const uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + rr) * (2 * a.I);
+          for (int q = 0; q < 16; ++q) {
+            const int r = 4 * (lane >> 5) + i * 32 + 8 * (q >> 2) + (q & 3);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            int col = nt * BN + wn * WN + j * 32 + (lane & 31);
-            col = col < a.N ? col : a.N - 1;
-            gv[qq][j] = gr[col];
-            uv[qq][j] = gr[a.I + col];
-          }
-        }
-        // all arithmetic before any store: no loaded value is used after a store
-        uint32_t gu_out[8][FN];  // grad_u << 16 | grad_g
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float ga = acc[i][j][8 * h + qq];
-            const float g = bf16_to_f32(gv[qq][j]), u = bf16_to_f32(uv[qq][j]);
-            const float sg = 1.0f / (1.0f + expf(-g));
-            gu_out[qq][j] = (uint32_t)to_bf16_bits(ga * u * (sg + g * sg * (1.0f - sg))) |
-                            ((uint32_t)to_bf16_bits(ga * (g * sg)) << 16);
-            pin(gu_out[qq][j]);
-          }
-#pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-          const int q = 8 * h + qq;
-          const int row = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-          if (row >= tr.rows) continue;
-          uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = nt * BN + wn * WN + j * 32 + (lane & 31);
-            if (col >= a.N) continue;
-            gr[col] = (uint16_t)(gu_out[qq][j] & 0xffffu);
-            gr[a.I + col] = (uint16_t)(gu_out[qq][j] >> 16);
+            for (int j = 0; j < FN; ++j) {
+              const int c = wn * WN + j * 32 + (lane & 31);
+              uint16_t* pg = (uint16_t*)(lg + at(r, c));
+              uint16_t* pu = (uint16_t*)(lu + at(r, c));
+              const float ga = acc[i][j][q];
+              const float g = bf16_to_f32(*pg), u = bf16_to_f32(*pu);
+              const float sg = 1.0f / (1.0f + expf(-g));
+              *pg = to_bf16_bits(ga * u * (sg + g * sg * (1.0f - sg)));
+              *pu = to_bf16_bits(ga * (g * sg));
+            }
           }
         }
       }
+      __syncthreads();
+      for (int ch = threadIdx.x; ch < WM * CPR; ch += blockDim.x) {
+        const int r = ch / CPR, c = (ch % CPR) * 8;
+        const int row = h * WM + r, col = nt * BN + c;
+        if (row >= tr.rows || col >= a.N) continue;
+        uint16_t* gr = a.gu + (int64_t)tr.joint_row(tr.v0 + row) * (2 * a.I);
+        *(uint4*)(gr + col) = *(const uint4*)(lg + at(r, c));
+        *(uint4*)(gr + a.I + col) = *(const uint4*)(lu + at(r, c));
+      }
+    }
     return;
   }
   // plain: the C tile goes through the freed stage buffers as row-major bf16
