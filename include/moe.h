@@ -36,9 +36,10 @@
  *    bf16, products accumulate in fp32, and act, y and out are each rounded to
  *    bf16 (nearest even) exactly once; silu uses the hardware exponential and
  *    reciprocal (relative error about 1e-7 * (1 + |z|), far below the bf16
- *    rounding).  dtype MOE_F32: fp32 everywhere.  Results do not depend on N,
- *    on the schedule or on the entry point used: every path gives the same
- *    bits.
+ *    rounding).  dtype MOE_F32: fp32 everywhere.  Forward results do not depend
+ *    on N, on the schedule or on the entry point used: every path gives the
+ *    same bits (the backward's fp32 weight gradients add the chunk pairs'
+ *    contributions in turn, so those depend on N within rounding).
  *  - Errors: the status comes from host-side checks of the arguments and of the
  *    kernel launches; nothing throws across the ABI.  Expert ids outside [0, E)
  *    are a device-side condition: such slots are dropped (no row, zero
