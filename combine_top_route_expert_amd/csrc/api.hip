@@ -58,7 +58,7 @@ FwdPlan fwd_plan(const Shape& s) {
 // to back so a pair uses them as joint buffers.
 struct BwdPlan {
   size_t counts, offsets, splits, src_row, dst_row, dev_err, meta_ws;
-  size_t xp[2], yg[2], act, gu;
+  size_t xp[2], yg[2], act, gu, order;
   size_t bytes;
   int nslots;
   MetaPlan meta;
@@ -88,6 +88,7 @@ BwdPlan bwd_plan(const Shape& s) {
   }
   p.act = take(p.nslots * rows * s.I * s.elem);
   p.gu = take(p.nslots * rows * 2 * s.I * s.elem);
+  p.order = take((size_t)s.E * 4);  // experts by rows, for the weight-gradient tiles
   p.bytes = o;
   return p;
 }
@@ -636,6 +637,10 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     dd.rows_bound = rows0 + rows1;
     st = dgrad(s, dd, s0);
     if (st != MOE_OK) return st;
+    // the weight-gradient tiles are dealt largest expert first
+    int32_t* order = (int32_t*)(w + p.order);
+    he = launch_expert_order(s, off0, off1, order, s0);
+    if (he != hipSuccess) return MOE_ERR_HIP;
     // W_d wgrad reads grad_y and act
     WgradIO wd{};
     wd.a[0] = yg0;
@@ -648,6 +653,7 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     wd.accumulate = first ? 0 : 1;
     wd.off[0] = off0;
     wd.off[1] = off1;
+    wd.order = order;
     st = wgrad(s, wd, s0);
     if (st != MOE_OK) return st;
     // gate/up dgrad: grad_x over y's (now free) buffer
@@ -678,6 +684,7 @@ moe_status moe_chunked_backward(const moe_shape* shape, const void* hidden_state
     wg.accumulate = first ? 0 : 1;
     wg.off[0] = off0;
     wg.off[1] = off1;
+    wg.order = order;
     st = wgrad(s, wg, s0);
     if (st != MOE_OK) return st;
     first = false;

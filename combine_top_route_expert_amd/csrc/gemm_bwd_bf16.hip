@@ -370,6 +370,7 @@ struct WgradArgs {
   const int32_t* off1;
   int E, M, N, m_tiles, n_tiles;
   int accumulate;    // 0: C = sum (experts without rows get zeros); 1: C += sum
+  const int32_t* order;  // nullable: experts in dealing order (largest first)
 };
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -390,7 +391,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   int emt, nt;
   if (!xcd_tile_rr(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
-  const int e = emt / a.m_tiles, mt = emt - e * a.m_tiles;
+  // tiles are dealt expert by expert, largest expert first when an order is
+  // given (the longest reductions start first, which shortens the tail)
+  const int rank = emt / a.m_tiles, mt = emt - rank * a.m_tiles;
+  const int e = a.order ? a.order[rank] : rank;
   TileRows tr;
   tr.e = e;
   tr.v0 = 0;
@@ -569,6 +573,34 @@ hipError_t launch_dgrad_bf16(const Shape& s, const DgradIO& io, hipStream_t st) 
   return hipGetLastError();
 }
 
+namespace {
+
+// order[rank] = expert: rank = number of experts with more rows, or as many
+// rows and a lower id.  One thread per expert, the row counts staged in LDS.
+__global__ void __launch_bounds__(1024) expert_order(const int32_t* __restrict__ off0,
+                                                     const int32_t* __restrict__ off1, int E,
+                                                     int32_t* __restrict__ order) {
+  __shared__ int rows[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    rows[e] = off0[e + 1] - off0[e] + (off1 ? off1[e + 1] - off1[e] : 0);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int n = rows[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (rows[f] > n || (rows[f] == n && f < e)) ? 1 : 0;
+    order[rank] = e;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_expert_order(const Shape& s, const int32_t* off0, const int32_t* off1,
+                               int32_t* order, hipStream_t st) {
+  if (s.E > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expert_order, dim3(1), dim3(1024), 0, st, off0, off1, s.E, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_wgrad_bf16(const Shape& s, const WgradIO& io, hipStream_t st) {
   WgradArgs a{};
   a.a.p[0] = (const uint16_t*)io.a[0];
@@ -586,6 +618,7 @@ hipError_t launch_wgrad_bf16(const Shape& s, const WgradIO& io, hipStream_t st) 
   a.M = io.M;
   a.N = io.N;
   a.accumulate = io.accumulate;
+  a.order = io.order;
   constexpr int BM = 256, BN = 256;
   a.m_tiles = (io.M + BM - 1) / BM;
   a.n_tiles = (io.N + BN - 1) / BN;

@@ -115,6 +115,7 @@ struct WgradArgsF {
   const int32_t* off0;
   const int32_t* off1;
   int E, M, N, m_tiles, n_tiles, accumulate;
+  const int32_t* order;  // nullable: experts in dealing order
 };
 
 __global__ void __launch_bounds__(kThreads) wgrad_gemm_f32(WgradArgsF a) {
@@ -123,7 +124,8 @@ __global__ void __launch_bounds__(kThreads) wgrad_gemm_f32(WgradArgsF a) {
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   int emt, nt;
   if (!xcd_tile_rr(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
-  const int e = emt / a.m_tiles, mt = emt - e * a.m_tiles;
+  const int rank = emt / a.m_tiles, mt = emt - rank * a.m_tiles;
+  const int e = a.order ? a.order[rank] : rank;
   TileRows tr;
   tr.e = e;
   tr.v0 = 0;
@@ -222,6 +224,7 @@ hipError_t launch_wgrad_f32(const Shape& s, const WgradIO& io, hipStream_t st) {
   a.M = io.M;
   a.N = io.N;
   a.accumulate = io.accumulate;
+  a.order = io.order;
   a.m_tiles = (io.M + BM - 1) / BM;
   a.n_tiles = (io.N + BN - 1) / BN;
   const int64_t grid = xcd_grid_rr((int64_t)s.E * a.m_tiles, a.n_tiles);

@@ -100,7 +100,14 @@ struct WgradIO {         // C[e] (+)= sum over e's rows v of A[v]^T B[v]
   int M, N;
   int accumulate;        // 0: overwrite (experts without rows get zeros), 1: add
   const int32_t* off[2];
+  // optional [E]: the experts in the order their tiles are dealt out (largest
+  // first, from launch_expert_order); null: expert order
+  const int32_t* order = nullptr;
 };
+// order[r] = the expert with the r-th most rows over one chunk or a pair (ties
+// to the lower id): one workgroup, E <= 1024.
+hipError_t launch_expert_order(const Shape& s, const int32_t* off0, const int32_t* off1,
+                               int32_t* order, hipStream_t st);
 hipError_t launch_dgrad_bf16(const Shape& s, const DgradIO& io, hipStream_t st);
 hipError_t launch_wgrad_bf16(const Shape& s, const WgradIO& io, hipStream_t st);
 hipError_t launch_dgrad_f32(const Shape& s, const DgradIO& io, hipStream_t st);
