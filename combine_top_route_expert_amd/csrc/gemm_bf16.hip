@@ -13,13 +13,18 @@
 // permute fused into the A loader's addresses.
 //
 // Pipeline: K advances BK (64) at a time.  Each stage of the A (rows) and B
-// (weight) tiles is copied global -> LDS by the direct-to-LDS load
-// (global_load_lds_dwordx4: 64 lanes x 16 bytes land as one contiguous 1 KB
-// block), so loads need no VGPRs and STAGES-1 stages are in flight while the
-// matrix cores work on the oldest one.  Completion is tracked with explicit
-// vmcnt waits plus a plain s_barrier (no fence that would drain every load).
-// LDS rows are XOR-swizzled (StageGeom) so that 16-byte fragment reads are free
-// of bank conflicts (measured).
+// (weight) tiles is copied HBM -> LDS by the direct-to-LDS load (64 lanes x 16
+// bytes land as one contiguous 1 KB block), so loads need no VGPRs and
+// STAGES-1 stages are in flight while the matrix cores work on the oldest one.
+// The buffer form of that load (a descriptor per operand, 32-bit offsets) is
+// used whenever the rows fit a 4 GiB window: with the global form, a FLAT
+// instruction, in flight, the compiler drains every LDS read before each MFMA
+// group; with descriptors it waits only for the fragments in use, and each
+// 16-deep sub-step's fragment reads overlap the previous sub-step's MFMAs
+// (gate/up 4-6% faster on the MFMA-bound workloads).  Completion is tracked
+// with explicit vmcnt waits plus a plain s_barrier (no fence that would drain
+// every load).  LDS rows are XOR-swizzled (StageGeom) so that 16-byte fragment
+// reads are free of bank conflicts (measured).
 //
 // Matrix instruction: on gfx950 v_mfma_f32_32x32x16_bf16 and
 // v_mfma_f32_16x16x32_bf16 both occupy the matrix pipe for about 32 cycles, so
@@ -92,7 +97,25 @@ struct GemmArgs {
   uint16_t* gu;               // gate_up, optional: g and u of each row, joint [rows][2I]
   const int32_t* gather[2];   // optional: A rows gathered from hidden_states (src_row slices)
   int gather_k;
+  const char* a_base;         // descriptor loads: every A row lies within 4 GiB above it
 };
+
+// Buffer descriptor of a raw byte range starting at p (stride 0, the largest
+// record count: offsets are computed from in-range rows, as for global loads).
+// (The host pass of the compiler has no buffer builtins; it never runs kernels.)
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, char* dst, uint32_t off, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, soff, 0, 0);
+}
+#else
+struct rsrc_t {};
+__device__ __forceinline__ rsrc_t raw_rsrc(const void*) { return {}; }
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t, char*, uint32_t, int) {}
+#endif
 
 // Address of virtual row v of the tile's expert on one side of the product.
 __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* const (&base)[2], int split,
@@ -143,7 +166,16 @@ struct StageGeom {
 };
 
 // Everything a workgroup needs to stream its tile's A and B stages into LDS.
-template <bool kGateUp, int BM, int BN, int NW, int WN, int BK>
+//
+// kBuf: the stages are copied with the buffer form of the direct-to-LDS load
+// (a descriptor per operand, 32-bit byte offsets per lane) instead of the
+// global form.  Same bytes, same LDS layout; but the global form is a FLAT
+// instruction, and while one is outstanding the compiler cannot count LDS
+// reads in order, so every wait for a fragment read drains all of them.  With
+// descriptor loads the K loop waits only for the fragments it is about to use,
+// and the next sub-step's reads overlap the current MFMAs.  The host picks the
+// global form when the A rows do not fit one 4 GiB window.
+template <bool kGateUp, int BM, int BN, int NW, int WN, int BK, bool kBuf>
 struct TileLoader {
   using G = StageGeom<BK>;
   static constexpr int LA = BM / G::RPB / NW, LB = BN / G::RPB / NW;  // 1 KB loads per wave
@@ -151,6 +183,8 @@ struct TileLoader {
   static_assert(LA * G::RPB * NW == BM && LB * G::RPB * NW == BN, "tile rows per wave");
   const char* a_src[LA];
   const char* b_src[LB];
+  uint32_t a_off[LA], b_off[LB];  // kBuf: byte offsets from the descriptors' bases
+  rsrc_t ra, rb;
   int wave, mrows;
   int live_a;  // A blocks of this wave that hold rows of the tile (the rest are skipped)
 
@@ -176,7 +210,8 @@ struct TileLoader {
       }
       live_a += (wave * LA + t) * G::RPB < mrows ? 1 : 0;
     }
-    const int e = tr.e;
+    // the expert is the same for the whole workgroup: keep its base scalar
+    const int e = __builtin_amdgcn_readfirstlane(tr.e);
     const uint16_t* Be = a.B + (int64_t)e * a.b_expert_stride;
 #pragma unroll
     for (int t = 0; t < LB; ++t) {
@@ -194,6 +229,28 @@ struct TileLoader {
       }
       b_src[t] = (const char*)(Be + (int64_t)brow * a.K + chunk * 8);
     }
+    if constexpr (kBuf) {
+      ra = raw_rsrc(a.a_base);
+      rb = raw_rsrc(Be);
+#pragma unroll
+      for (int t = 0; t < LA; ++t) a_off[t] = (uint32_t)(a_src[t] - a.a_base);
+#pragma unroll
+      for (int t = 0; t < LB; ++t) b_off[t] = (uint32_t)(b_src[t] - (const char*)Be);
+    }
+  }
+
+  // One 1 KB block: 64 lanes x 16 bytes at byte koff of their rows into dst.
+  __device__ __forceinline__ void load_a(int t, int koff, char* dst) const {
+    if constexpr (kBuf)
+      buffer_load_lds16(ra, dst, a_off[t], koff);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff), (lds_void*)dst, 16, 0, 0);
+  }
+  __device__ __forceinline__ void load_b(int t, int koff, char* dst) const {
+    if constexpr (kBuf)
+      buffer_load_lds16(rb, dst, b_off[t], koff);
+    else
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + koff), (lds_void*)dst, 16, 0, 0);
   }
 
   // Compact stage of a tile with at most SROWS rows: those rows of A (the
@@ -205,17 +262,13 @@ struct TileLoader {
   template <int SROWS>
   __device__ __forceinline__ void issue_small(char* smem, int kt, int buf) const {
     char* base = smem + buf * small_stage<SROWS>();
-    const int64_t koff = (int64_t)kt * G::ROW_BYTES;
+    const int koff = kt * G::ROW_BYTES;
 #pragma unroll
     for (int t = 0; t < LA; ++t)
       if (t < live_a)  // blocks past the tile's (at most SROWS) rows are not live
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff),
-                                         (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+        load_a(t, koff, base + (wave * LA + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < LB; ++t)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(b_src[t] + koff),
-          (lds_void*)(base + small_a<SROWS>() + (wave * LB + t) * 1024), 16, 0, 0);
+    for (int t = 0; t < LB; ++t) load_b(t, koff, base + small_a<SROWS>() + (wave * LB + t) * 1024);
   }
 
   // Loads one stage.  A blocks of 1 KB that lie wholly past the tile's rows are
@@ -223,17 +276,12 @@ struct TileLoader {
   // wave issues live_a + LB loads per stage.
   __device__ __forceinline__ void issue(char* smem, int kt, int buf) const {
     char* base = smem + buf * STAGE_BYTES;
-    const int64_t koff = (int64_t)kt * G::ROW_BYTES;
+    const int koff = kt * G::ROW_BYTES;
 #pragma unroll
     for (int t = 0; t < LA; ++t)
-      if (t < live_a)
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff),
-                                         (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+      if (t < live_a) load_a(t, koff, base + (wave * LA + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < LB; ++t)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(b_src[t] + koff),
-          (lds_void*)(base + BM * G::ROW_BYTES + (wave * LB + t) * 1024), 16, 0, 0);
+    for (int t = 0; t < LB; ++t) load_b(t, koff, base + BM * G::ROW_BYTES + (wave * LB + t) * 1024);
   }
 };
 
@@ -331,32 +379,47 @@ template <int F, int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, cla
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
                                        int KT, int per_stage, int lane, int wm, int wn) {
   using G = StageGeom<BK>;
+  constexpr int KS = BK / 16;  // MFMA sub-steps per stage
+  // nothing of the lgkm class (scalar loads included) is pending on entry, so
+  // the waits before each sub-step's MFMAs can count the LDS reads in order
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed once only the newer stages issued so far are pending
     const int newer = KT - 1 - kt < STAGES - 2 ? KT - 1 - kt : STAGES - 2;
     wait_loads(newer * per_stage);
     __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     const char* sa = smem + (kt % STAGES) * Loader::STAGE_BYTES;
     const char* sb = sa + BM * G::ROW_BYTES;
     if constexpr (F > 0) {
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
+      // fragments in two register sets: sub-step kk + 1 is read while the
+      // MFMAs of sub-step kk run
+      bf16x8 af[2][F], bfr[2][FN];
+      auto frag = [&](int kk, int b) __attribute__((always_inline)) {
         const int fo = G::frag_offset(lane, kk);
-        bf16x8 af[F], bfr[FN];
 #pragma unroll
         for (int i = 0; i < F; ++i)
-          af[i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * G::ROW_BYTES + fo);
+          af[b][i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * G::ROW_BYTES + fo);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+          bfr[b][j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+      };
+      frag(0, 0);  // ahead of the next stage's loads, so the first MFMAs start sooner
+      if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) frag(kk + 1, (kk + 1) & 1);
+        // keeps the compiler from sinking those reads below this sub-step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < F; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+      if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     }
     // this stage's LDS reads are complete before any wave refills its buffer
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -408,12 +471,12 @@ __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader
 }
 
 template <bool kGateUp, bool kSaveGU, int BM, int BN, int WAVES_M, int WAVES_N, int BK,
-          int STAGES>
+          int STAGES, bool kBuf>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(GemmArgs a) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
-  using Loader = TileLoader<kGateUp, BM, BN, NW, WN, BK>;
+  using Loader = TileLoader<kGateUp, BM, BN, NW, WN, BK, kBuf>;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(!kGateUp || WN % 64 == 0, "gate/up halves");
   static_assert(STAGES >= 2, "pipeline depth");
@@ -510,7 +573,8 @@ enum Instance { kAuto = 0, kWide = 1, kNarrow = 2 };
 // weight streaming.
 bool prefer_wide(int64_t rows_bound) { return rows_bound >= 4096; }
 
-template <bool kGateUp, bool kSaveGU, int BM, int BN, int WM_, int WN_, int BK, int ST>
+template <bool kGateUp, bool kSaveGU, int BM, int BN, int WM_, int WN_, int BK, int ST,
+          bool kBuf>
 hipError_t launch_instance(GemmArgs a, const Shape& s, int64_t rows_bound, hipStream_t st) {
   constexpr int threads = 64 * WM_ * WN_;
   // gate_up tiles cover BN/2 intermediate columns (gate and up halves)
@@ -518,12 +582,12 @@ hipError_t launch_instance(GemmArgs a, const Shape& s, int64_t rows_bound, hipSt
   const int64_t grid = xcd_grid(m_tiles_bound(rows_bound, s.E, BM), a.n_tiles);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((grouped_gemm_bf16<kGateUp, kSaveGU, BM, BN, WM_, WN_, BK, ST>),
+  hipLaunchKernelGGL((grouped_gemm_bf16<kGateUp, kSaveGU, BM, BN, WM_, WN_, BK, ST, kBuf>),
                      dim3((unsigned)grid), dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
-template <bool kGateUp, bool kSaveGU>
+template <bool kGateUp, bool kSaveGU, bool kBuf>
 hipError_t launch_kind(int inst, GemmArgs a, const Shape& s, int64_t rows_bound, hipStream_t st) {
   // a 256-column gate_up tile holds 128 intermediate columns
   const bool wide_ok = !kGateUp || s.I % 128 == 0;
@@ -531,8 +595,37 @@ hipError_t launch_kind(int inst, GemmArgs a, const Shape& s, int64_t rows_bound,
     inst = prefer_wide(rows_bound) ? kWide : kNarrow;
   }
   if (inst == kWide && wide_ok)
-    return launch_instance<kGateUp, kSaveGU, 256, 256, 2, 4, 64, 2>(a, s, rows_bound, st);
-  return launch_instance<kGateUp, kSaveGU, 64, 128, 2, 2, 64, 2>(a, s, rows_bound, st);
+    return launch_instance<kGateUp, kSaveGU, 256, 256, 2, 4, 64, 2, kBuf>(a, s, rows_bound, st);
+  return launch_instance<kGateUp, kSaveGU, 64, 128, 2, 2, 64, 2, kBuf>(a, s, rows_bound, st);
+}
+
+template <bool kGateUp, bool kSaveGU>
+hipError_t launch_kind(bool buf, int inst, GemmArgs a, const Shape& s, int64_t rows_bound,
+                       hipStream_t st) {
+  return buf ? launch_kind<kGateUp, kSaveGU, true>(inst, a, s, rows_bound, st)
+             : launch_kind<kGateUp, kSaveGU, false>(inst, a, s, rows_bound, st);
+}
+
+// Descriptor loads take 32-bit byte offsets: every A row (a row of
+// hidden_states when gathered, else of one or both row buffers, each bounded
+// by the launch's rows) must lie within 4 GiB above the lowest base, and each
+// expert's weight block within 4 GiB of its start.  Sets a.a_base.
+bool descriptor_loads_fit(GemmArgs& a, const Shape& s, int64_t rows_bound) {
+  const uint64_t row_bytes = (uint64_t)a.K * 2;
+  const uint64_t a0 = (uint64_t)(uintptr_t)a.A[0], a1 = (uint64_t)(uintptr_t)a.A[1];
+  uint64_t lo = a0, hi;
+  if (a.gather[0]) {
+    hi = a0 + (uint64_t)s.T * row_bytes;
+  } else {
+    hi = a0 + (uint64_t)rows_bound * row_bytes;
+    if (a.a_split) {
+      lo = std::min(a0, a1);
+      hi = std::max(hi, a1 + (uint64_t)rows_bound * row_bytes);
+    }
+  }
+  a.a_base = (const char*)(uintptr_t)lo;
+  const uint64_t lim = (uint64_t)1 << 32;
+  return hi - lo < lim && (uint64_t)a.b_expert_stride * 2 < lim;
 }
 
 hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void* B,
@@ -562,13 +655,15 @@ hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void*
     a.b_expert_stride = (int64_t)2 * s.I * s.H;
     // the backward's recompute also saves g and u (its own instance, so the
     // forward kernel keeps its registers)
-    if (a.gu) return launch_kind<true, true>(inst, a, s, rows_bound, st);
-    return launch_kind<true, false>(inst, a, s, rows_bound, st);
+    const bool buf = descriptor_loads_fit(a, s, rows_bound);
+    if (a.gu) return launch_kind<true, true>(buf, inst, a, s, rows_bound, st);
+    return launch_kind<true, false>(buf, inst, a, s, rows_bound, st);
   }
   a.K = s.I;
   a.ncols = s.H;
   a.b_expert_stride = (int64_t)s.H * s.I;
-  return launch_kind<false, false>(inst, a, s, rows_bound, st);
+  const bool buf = descriptor_loads_fit(a, s, rows_bound);
+  return launch_kind<false, false>(buf, inst, a, s, rows_bound, st);
 }
 
 }  // namespace

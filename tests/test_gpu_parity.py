@@ -311,6 +311,45 @@ def test_expert_ffn_pair_bitwise(name, N, c):
     assert torch.equal(act2, act)
 
 
+@pytest.mark.parametrize("name,N", [("bf16_e64_zipf", 2), ("odd_dims_bf16", 3)])
+def test_gate_up_pair_rows_over_4gib_apart(name, N):
+    """The pair gate/up copies its stages with 32-bit offsets from one base when
+    both chunks' rows fit a 4 GiB window, else with 64-bit addresses: two row
+    buffers more than 4 GiB apart take the second form and must give the same
+    bits as the same rows side by side (256x256 tile for the Zipf workload,
+    64x128 for the odd sizes)."""
+    L = layer_for(name)
+    cfg = L.cfg
+    shape = L.shape(N)
+    meta = run_route_meta(L.idx, shape)
+    dst = torch.from_numpy(meta["dst_row"]).cuda()
+    off = torch.from_numpy(meta["offsets"]).cuda()
+    dt = cfg.torch_dtype
+    n = []
+    for cc in (0, 1):
+        t0, t1 = moe.moe_chunk_range(shape, cc)
+        n.append((t1 - t0) * cfg.k)
+    row_bytes = cfg.H * 2
+    gap = (1 << 32) + 4096
+    big = torch.empty(n[0] * row_bytes + gap + n[1] * row_bytes, dtype=torch.uint8, device="cuda")
+    far = [big[:n[0] * row_bytes].view(dt).view(n[0], cfg.H),
+           big[n[0] * row_bytes + gap:].view(dt).view(n[1], cfg.H)]
+    near = torch.empty((n[0] + n[1], cfg.H), dtype=dt, device="cuda")
+    near = [near[:n[0]], near[n[0]:]]
+    for cc in (0, 1):
+        moe.moe_permute(shape, cc, L.hidden, dst, near[cc])
+        far[cc].copy_(near[cc])
+    acts = []
+    for xs in (near, far):
+        act = torch.full((n[0] + n[1], cfg.I), 555.0, dtype=dt, device="cuda")
+        say(f"gate_up_pair {name} N={N} rows {'far apart' if xs is far else 'adjacent'}")
+        moe.moe_expert_gate_up_pair(shape, 0, xs[0], xs[1], off, L.wgu, act)
+        acts.append(act)
+    torch.cuda.synchronize()
+    assert torch.equal(acts[0], acts[1])
+    del big
+
+
 def test_run_twice_identical():
     L = layer_for("packed16k_e128")
     a, _ = run_forward(L, L.shape(2))
