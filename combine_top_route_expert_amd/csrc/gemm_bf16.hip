@@ -100,22 +100,6 @@ struct GemmArgs {
   const char* a_base;         // descriptor loads: every A row lies within 4 GiB above it
 };
 
-// Buffer descriptor of a raw byte range starting at p (stride 0, the largest
-// record count: offsets are computed from in-range rows, as for global loads).
-// (The host pass of the compiler has no buffer builtins; it never runs kernels.)
-#if defined(__HIP_DEVICE_COMPILE__)
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t raw_rsrc(const void* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
-}
-__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, char* dst, uint32_t off, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, soff, 0, 0);
-}
-#else
-struct rsrc_t {};
-__device__ __forceinline__ rsrc_t raw_rsrc(const void*) { return {}; }
-__device__ __forceinline__ void buffer_load_lds16(rsrc_t, char*, uint32_t, int) {}
-#endif
 
 // Address of virtual row v of the tile's expert on one side of the product.
 __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* const (&base)[2], int split,
@@ -608,24 +592,13 @@ hipError_t launch_kind(bool buf, int inst, GemmArgs a, const Shape& s, int64_t r
 
 // Descriptor loads take 32-bit byte offsets: every A row (a row of
 // hidden_states when gathered, else of one or both row buffers, each bounded
-// by the launch's rows) must lie within 4 GiB above the lowest base, and each
+// by the launch's rows) must lie within 4 GiB above the lower base, and each
 // expert's weight block within 4 GiB of its start.  Sets a.a_base.
 bool descriptor_loads_fit(GemmArgs& a, const Shape& s, int64_t rows_bound) {
-  const uint64_t row_bytes = (uint64_t)a.K * 2;
-  const uint64_t a0 = (uint64_t)(uintptr_t)a.A[0], a1 = (uint64_t)(uintptr_t)a.A[1];
-  uint64_t lo = a0, hi;
-  if (a.gather[0]) {
-    hi = a0 + (uint64_t)s.T * row_bytes;
-  } else {
-    hi = a0 + (uint64_t)rows_bound * row_bytes;
-    if (a.a_split) {
-      lo = std::min(a0, a1);
-      hi = std::max(hi, a1 + (uint64_t)rows_bound * row_bytes);
-    }
-  }
-  a.a_base = (const char*)(uintptr_t)lo;
-  const uint64_t lim = (uint64_t)1 << 32;
-  return hi - lo < lim && (uint64_t)a.b_expert_stride * 2 < lim;
+  const uint16_t* a1 = a.a_split ? a.A[1] : a.A[0];
+  a.a_base = (const char*)std::min(a.A[0], a1);
+  return rows_fit_4g(a.A[0], a1, a.gather[0] ? s.T : rows_bound, a.K) &&
+         (uint64_t)a.b_expert_stride * 2 < ((uint64_t)1 << 32);
 }
 
 hipError_t launch(bool gate_up, const Shape& s, const GroupedIO& io, const void* B,

@@ -25,6 +25,36 @@ inline void chunk_tokens(const Shape& s, int c, int* t0, int* t1) {
   *t1 = (int)(b < s.T ? b : s.T);
 }
 
+// ---- direct-to-LDS loads through buffer descriptors (GEMM kernels) ----------
+// A raw descriptor of the bytes above p (stride 0, the largest record count:
+// offsets are computed from in-range rows, as for global loads) and the 16-byte
+// direct-to-LDS load through it: lane l's 16 bytes at off + soff land at
+// dst + 16 l.  The host pass of the compiler has no buffer builtins (it never
+// runs kernels), hence the empty stand-ins there.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t r, char* dst, uint32_t off, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           off, soff, 0, 0);
+}
+#else
+struct rsrc_t {};
+__device__ __forceinline__ rsrc_t raw_rsrc(const void*) { return {}; }
+__device__ __forceinline__ void buffer_load_lds16(rsrc_t, char*, uint32_t, int) {}
+#endif
+
+// Host: whether rows of ld 2-byte elements in the buffers at p0 and p1 (at
+// most `rows` rows each) lie within 4 GiB above the lower base, so that
+// descriptor loads from that base reach them with 32-bit offsets.
+inline bool rows_fit_4g(const void* p0, const void* p1, int64_t rows, int64_t ld) {
+  const uint64_t a = (uint64_t)(uintptr_t)p0, b = (uint64_t)(uintptr_t)p1;
+  const uint64_t lo = a < b ? a : b, hi = (a > b ? a : b) + (uint64_t)rows * ld * 2;
+  return hi - lo < ((uint64_t)1 << 32);
+}
+
 // ---- routing metadata (meta.hip) -------------------------------------------
 constexpr int kMaxExperts = 1024;  // largest E the library accepts
 constexpr int kMetaSeg = 256;      // segment granule, in assignments (one wave per segment)
