@@ -51,7 +51,7 @@
 // Epilogue: the accumulators go through the freed stage buffers as a
 // row-major bf16 tile and leave as 16-byte row segments (store_tile_lds).
 //
-// Small tiles: an m-tile of at most 32 or 64 rows (a small expert's only
+// Small tiles: an m-tile of at most 32, 64 or 128 rows (a small expert's only
 // tile) has little MFMA work and is bound by streaming its weight panel, so it
 // runs a K loop with a compact stage layout (its rows of A, then B) and three
 // stages, two in flight (k_loop_small): 41 -> 33 us per gate/up tile of at
@@ -467,8 +467,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   static_assert((STAGES - 2) * (Loader::LA + Loader::LB) <= 24, "wait_loads range");
   constexpr int kSmemBytes =
       cmax(STAGES * Loader::STAGE_BYTES,
-           FM >= 4 ? cmax(3 * Loader::template small_stage<32>(),
-                          3 * Loader::template small_stage<64>())
+           FM >= 4 ? cmax(3 * Loader::template small_stage<128>(),
+                          cmax(3 * Loader::template small_stage<32>(),
+                               3 * Loader::template small_stage<64>()))
                    : 0);
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 
@@ -493,8 +494,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
   const int KT = a.K / BK;
-  // tiles of at most 32 or 64 rows: three compact stages (a fourth stage for
-  // the 32-row tiles, in 16 KB more LDS, measured no faster)
+  // tiles of at most 32, 64 or 128 rows: three compact stages (a fourth stage
+  // for the 32-row tiles, in 16 KB more LDS, measured no faster; the 128-row
+  // case, 144 KB, took the DeepSeek-V3-shaped layer's gate/up from 3.18 to
+  // 3.01 ms, its experts holding 95-160 rows each)
   constexpr bool kSmallPath = FM >= 4 && WAVES_M == 2;
   if (kSmallPath && tr.rows <= 32) {
     if (wm == 0)
@@ -506,6 +509,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       k_loop_small<true, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
     else
       k_loop_small<false, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+  } else if (kSmallPath && tr.rows <= 128) {
+    if (wm == 0)
+      k_loop_small<true, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+    else
+      k_loop_small<false, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
   } else {
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
