@@ -356,7 +356,7 @@ def main():
     log(f"backward N={N}")
     bwd_ms, bwd_ws = time_backward(moe, torch, shape, inp, max(5, args.steps // 5), 2)
     log("per-kernel timing")
-    kt, rows0, e_act0, _ = kernel_times(moe, torch, shape, inp, args.kernel_reps)
+    kt, rows0, e_act0, chunk_rows = kernel_times(moe, torch, shape, inp, args.kernel_reps)
     copy_bw = copy_bandwidth(torch)
 
     s = cfg.elem_bytes
@@ -387,6 +387,27 @@ def main():
     roof["avg_launch_us"] = kt["gate_up"]
     roof["mfma_frac"] = gu_flops / gu_s / peak_f
 
+    # every launch the layer makes for its first chunk pair, against its own
+    # roofline: algorithmic bytes (and flop) per launch / the launch's time
+    tok0 = chunk_rows[0] // cfg.k  # tokens of chunk 0
+    dn_bytes = rows0 * I * s + e_act0 * H * I * s + rows0 * H * s
+    per_kernel = {
+        "route_meta": (12 * cfg.T * cfg.k, 0.0, "all chunks: ids read twice, src_row and dst_row"),
+        "permute": (tok0 * H * s + chunk_rows[0] * H * s + 4 * chunk_rows[0], 0.0,
+                    "chunk 0 (per-chunk schedule; the pair-fused layer gathers in gate_up)"),
+        "gate_up": (gu_bytes, gu_flops, "chunks 0-1, rows gathered from hidden_states"),
+        "down": (dn_bytes, 2.0 * rows0 * H * I, "chunks 0-1"),
+        "combine": (chunk_rows[0] * H * s + tok0 * H * s + 8 * chunk_rows[0], 0.0, "chunk 0"),
+    }
+    kernels_roofline = {}
+    for name, (nbytes, flop, what) in per_kernel.items():
+        sec = kt[name] * 1e-6
+        r = {"us": kt[name], "bytes": nbytes, "GBps": nbytes / sec / 1e9,
+             "hbm_frac": nbytes / sec / HBM_PEAK, "launch": what}
+        if flop:
+            r.update({"flop": flop, "TFLOPs": flop / sec / 1e12, "mfma_frac": flop / sec / peak_f})
+        kernels_roofline[name] = r
+
     ms = main_run["wall_ms"]
     line = {
         "metric": METRIC, "value": cfg.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -397,6 +418,7 @@ def main():
                    "groups": cfg.groups},
         "roofline": roof,
         "kernels_us": kt,
+        "kernels_roofline": kernels_roofline,
         "event_ms_per_step": main_run["event_ms"],
         "unchunked": {"ms_per_step": run1["wall_ms"], "value": cfg.T / (run1["wall_ms"] * 1e-3)},
         "per_chunk_schedule": {"ms_per_step": run_pc["wall_ms"],
