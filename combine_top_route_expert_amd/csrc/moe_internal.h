@@ -336,8 +336,11 @@ struct MTileMap {
 // which shortens the tail of the launch.  Every m-tile comes with all its
 // n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
 // those past their XCD's share exit.
-__device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* mt, int* nt) {
-  const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+// xcd_tile_at: the same for position q of XCD x's sequence (a workgroup that
+// takes several tiles walks q, q + G, q + 2G, ... with G its XCD's workgroup
+// count); false once q is past the XCD's tiles.
+__device__ __forceinline__ bool xcd_tile_at(const MTileMap& tm, int n_tiles, int x, int q,
+                                            int* mt, int* nt) {
   const int ml = q / n_tiles;
   *nt = q - ml * n_tiles;
   const int per = (tm.large + 7) >> 3;
@@ -377,6 +380,10 @@ __device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* m
   const int p = j < deficit ? before + j : D + (j - deficit) * 8 + x;
   *mt = tm.large + p;
   return *mt < tm.total;
+}
+
+__device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* mt, int* nt) {
+  return xcd_tile_at(tm, n_tiles, blockIdx.x & 7, blockIdx.x >> 3, mt, nt);
 }
 
 // Round-robin variant: XCD x takes m-tiles x, x + 8, x + 16, ... (each with all
