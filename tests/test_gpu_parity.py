@@ -249,6 +249,26 @@ def test_chunked_equals_unchunked_bitwise(name, Ns):
                 assert torch.equal(out, base), (N, sched, two)
 
 
+def test_tile_loop_several_tiles_per_workgroup():
+    """4096 rows over E = 256 mostly small experts: the 256x256 grouped GEMMs
+    run their tile-loop variant with the grid capped to 128 workgroups per XCD,
+    so every workgroup takes several m-tiles (about 4 for gate/up, 7 for down).
+    N = 4 runs pairs of 2048 rows with the 64x128 one-tile kernel.  The two
+    outputs must be the same bits, and sampled tokens must match the oracle."""
+    L = layer_for("decode_t64", 512)
+    cfg = L.cfg
+    say("tile loop: decode shape T=512 N=1")
+    base, err = run_forward(L, L.shape(1), two_streams=False)
+    assert err == 0
+    say("tile loop: decode shape T=512 N=4")
+    out4, _ = run_forward(L, L.shape(4), two_streams=False)
+    assert torch.equal(out4, base)
+    toks = sample_tokens(cfg.T, 12)
+    ref = oracle.moe_tokens(toks, L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I)
+    e = oracle.row_rel_err(f64(base[toks]), ref)
+    assert e <= 2e-2, e
+
+
 PAIR_CASES = [("bf16_e64_zipf", 2, 0), ("tiny_f32", 3, 0), ("tiny_f32", 3, 2), ("t3_n4", 4, 2),
               ("packed16k_e128", 4, 2), ("dsv3_e256", 3, 0), ("dsv3_e256", 3, 2),
               ("decode_t64", 2, 0)]
