@@ -484,80 +484,80 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   // thousands of workgroups that find none).
   const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
   for (int q = blockIdx.x >> 3;; q += wg_per_xcd) {
-  // (built per tile: kept across the K loop it would cost registers)
-  MTileMap tm;
-  // the wide tile (one workgroup per CU) orders small experts' m-tiles by size
-  // to balance the XCDs; the narrow tile (three per CU) keeps expert order,
-  // which mixes weight-streaming and MFMA-bound tiles on a CU (measured faster)
-  tm.build(a.off0, a.off1, a.E, BM, BM >= 128 ? BM : 1);
-  int mt, nt;
-  if (!xcd_tile_at(tm, a.n_tiles, xcd, q, &mt, &nt)) break;
-  const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
-  Loader ld;
-  ld.init(a, tr, nt, lane, wave);
-  const int per_stage = ld.live_a + Loader::LB;  // loads this wave issues per stage
+    // (built per tile: kept across the K loop it would cost registers)
+    MTileMap tm;
+    // the wide tile (one workgroup per CU) orders small experts' m-tiles by size
+    // to balance the XCDs; the narrow tile (three per CU) keeps expert order,
+    // which mixes weight-streaming and MFMA-bound tiles on a CU (measured faster)
+    tm.build(a.off0, a.off1, a.E, BM, BM >= 128 ? BM : 1);
+    int mt, nt;
+    if (!xcd_tile_at(tm, a.n_tiles, xcd, q, &mt, &nt)) break;
+    const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
+    Loader ld;
+    ld.init(a, tr, nt, lane, wave);
+    const int per_stage = ld.live_a + Loader::LB;  // loads this wave issues per stage
 
-  f32x16 acc[FM][FN];
+    f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  const int KT = a.K / BK;
-  // tiles of at most 32, 64 or 128 rows: three compact stages (a fourth stage
-  // for the 32-row tiles, in 16 KB more LDS, measured no faster; the 128-row
-  // case, 144 KB, took the DeepSeek-V3-shaped layer's gate/up from 3.18 to
-  // 3.01 ms, its experts holding 95-160 rows each)
-  constexpr bool kSmallPath = FM >= 4 && WAVES_M == 2;
-  if (kSmallPath && tr.rows <= 32) {
-    if (wm == 0)
-      k_loop_small<true, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-    else
-      k_loop_small<false, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-  } else if (kSmallPath && tr.rows <= 64) {
-    if (wm == 0)
-      k_loop_small<true, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-    else
-      k_loop_small<false, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-  } else if (kSmallPath && tr.rows <= 128) {
-    if (wm == 0)
-      k_loop_small<true, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-    else
-      k_loop_small<false, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-  } else {
+    const int KT = a.K / BK;
+    // tiles of at most 32, 64 or 128 rows: three compact stages (a fourth stage
+    // for the 32-row tiles, in 16 KB more LDS, measured no faster; the 128-row
+    // case, 144 KB, took the DeepSeek-V3-shaped layer's gate/up from 3.18 to
+    // 3.01 ms, its experts holding 95-160 rows each)
+    constexpr bool kSmallPath = FM >= 4 && WAVES_M == 2;
+    if (kSmallPath && tr.rows <= 32) {
+      if (wm == 0)
+        k_loop_small<true, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+      else
+        k_loop_small<false, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+    } else if (kSmallPath && tr.rows <= 64) {
+      if (wm == 0)
+        k_loop_small<true, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+      else
+        k_loop_small<false, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+    } else if (kSmallPath && tr.rows <= 128) {
+      if (wm == 0)
+        k_loop_small<true, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+      else
+        k_loop_small<false, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+    } else {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) ld.issue(smem, s, s);
-  // 32-row blocks of this wave's band that hold rows of the tile.  Blocks past
-  // them feed only outputs that are never stored, so a wide tile skips their
-  // MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block loop, 3 runs
-  // the full one).  A one-block band always runs its MFMAs: a wave-uniform
-  // branch there measured slower than the wasted work.
-  const int band_rows = tr.rows - wm * WM;
-  const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < KT) ld.issue(smem, s, s);
+      // 32-row blocks of this wave's band that hold rows of the tile.  Blocks past
+      // them feed only outputs that are never stored, so a wide tile skips their
+      // MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block loop, 3 runs
+      // the full one).  A one-block band always runs its MFMAs: a wave-uniform
+      // branch there measured slower than the wasted work.
+      const int band_rows = tr.rows - wm * WM;
+      const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
 #define MOE_K_LOOP(F) \
-  k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
-  if constexpr (FM == 1) {
-    MOE_K_LOOP(1);
-  } else {
-    if (fm_live > 2)
-      MOE_K_LOOP(FM);
-    else if (fm_live == 2)
-      MOE_K_LOOP(2);
-    else if (fm_live == 1)
-      MOE_K_LOOP(1);
-    else
-      MOE_K_LOOP(0);
-  }
+      k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
+      if constexpr (FM == 1) {
+        MOE_K_LOOP(1);
+      } else {
+        if (fm_live > 2)
+          MOE_K_LOOP(FM);
+        else if (fm_live == 2)
+          MOE_K_LOOP(2);
+        else if (fm_live == 1)
+          MOE_K_LOOP(1);
+        else
+          MOE_K_LOOP(0);
+      }
 #undef MOE_K_LOOP
-  }
-  static_assert(BM * (kGateUp ? BN / 2 : BN) * 2 <= STAGES * Loader::STAGE_BYTES,
-                "C tile fits the stage buffers");
-  __syncthreads();  // every wave is done with the stage buffers
-  store_tile_lds<kGateUp, kSaveGU ? 3 : 1, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, wm, wn,
-                                                                           lane, smem);
-  if constexpr (!kLoop) break;
-  __syncthreads();  // the C tile has left LDS before the next tile's stage loads
+    }
+    static_assert(BM * (kGateUp ? BN / 2 : BN) * 2 <= STAGES * Loader::STAGE_BYTES,
+                  "C tile fits the stage buffers");
+    __syncthreads();  // every wave is done with the stage buffers
+    store_tile_lds<kGateUp, kSaveGU ? 3 : 1, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, wm, wn,
+                                                                             lane, smem);
+    if constexpr (!kLoop) break;
+    __syncthreads();  // the C tile has left LDS before the next tile's stage loads
   }
 }
 
