@@ -217,6 +217,28 @@ def test_forward_every_row_vs_oracle(name, N, T):
     assert e <= TOL[cfg.dtype], e
 
 
+@pytest.mark.parametrize("name,kw", [
+    ("odd_dims_bf16", dict(T=50, k=64, E=96, H=128, I=128, groups=2)),
+    ("odd_dims_f32", dict(T=29, k=64, E=70, H=36, I=20, groups=1)),
+])
+def test_forward_largest_top_k(name, kw):
+    """top_k = 64, the largest the library accepts: each token's combine sums 64
+    rows.  Every row against the oracle; chunked (N = 3) equals unchunked bit
+    for bit."""
+    cfg = C[name].with_(**kw)
+    L = build_layer(cfg)
+    say(f"top_k=64 {name} N=1")
+    out, err = run_forward(L, L.shape(1))
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, 1)
+    assert err == meta["n_invalid"] == 0
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL[cfg.dtype], e
+    say(f"top_k=64 {name} N=3")
+    out3, _ = run_forward(L, L.shape(3))
+    assert torch.equal(out3, out)
+
+
 SAMPLED_CASES = [("bf16_e64_zipf", 2, 24), ("dsv3_e256", 1, 4), ("packed16k_e128", 4, 48),
                  ("packed16k_e128", 8, 16), ("decode_t64", 1, 6), ("skew_two_experts", 1, 64)]
 
