@@ -239,6 +239,26 @@ def test_forward_largest_top_k(name, kw):
     assert torch.equal(out3, out)
 
 
+def test_forward_largest_expert_count():
+    """E = 1024, the largest the library accepts, 4800 rows: the tile map
+    numbers 16 experts per lane, the 256x256 gate/up runs its tile-loop form
+    (the bound counts up to 1024 partial m-tiles) and the down its one-tile
+    form; N = 4 runs pairs of 2400 rows with the 64x128 kernel.  Every row
+    against the oracle; both give the same bits."""
+    cfg = C["odd_dims_bf16"].with_(T=600, k=8, E=1024, H=128, I=256, groups=16)
+    L = build_layer(cfg)
+    say("E=1024 N=1")
+    out, err = run_forward(L, L.shape(1))
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, 1)
+    assert err == meta["n_invalid"] == 0
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL[cfg.dtype], e
+    say("E=1024 N=4")
+    out4, _ = run_forward(L, L.shape(4))
+    assert torch.equal(out4, out)
+
+
 SAMPLED_CASES = [("bf16_e64_zipf", 2, 24), ("dsv3_e256", 1, 4), ("packed16k_e128", 4, 48),
                  ("packed16k_e128", 8, 16), ("decode_t64", 1, 6), ("skew_two_experts", 1, 64)]
 
