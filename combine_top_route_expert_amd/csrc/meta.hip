@@ -22,6 +22,17 @@
 //     plus the segment's running base per expert gives dst_row[f] and
 //     src_row[chunk_start + row] = f.  Lanes are walked in ascending f, so the
 //     permutation is stable.
+//
+// Chunks of at most kFusedMaxIds assignments (E <= kFusedMaxE, at most
+// kFusedMaxAll assignments in all) take one launch instead: meta_fused runs
+// the same three steps in one 1024-thread workgroup per chunk.  Wave w owns
+// the w-th of 16 contiguous slices of the chunk (at most 512 assignments, held
+// in registers with their peer masks from the histogram pass to the rank pass)
+// and keeps its per-expert counts in row w of LDS, so the prefix over slices
+// takes the place of the prefix over segments and no step waits on another
+// launch.  Workgroup 0 also counts the dropped ids of every chunk.  Chunks this
+// small are latency-bound: the two extra launches and the round trip of the
+// segment counts through memory cost more than the work.
 #include "moe_internal.h"
 
 namespace moe {
@@ -248,6 +259,113 @@ __global__ void __launch_bounds__(64) meta_rank(MetaArgs a) {
   }
 }
 
+constexpr int kFusedWaves = 16;
+constexpr int kFusedMaxE = 512;       // LDS: kFusedWaves * E counters
+constexpr int kFusedMaxIds = 8192;    // assignments of one chunk
+constexpr int64_t kFusedMaxAll = 65536;  // all chunks (workgroup 0 counts dropped ids)
+
+__global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
+  __shared__ int cnt[kFusedWaves * kFusedMaxE];  // [slice][E]
+  __shared__ int off_lds[kFusedMaxE + 1];
+  __shared__ int lds_waves[48];
+  const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
+  if (t0 > a.T) t0 = a.T;
+  if (t1 > a.T) t1 = a.T;
+  const int f0 = (int)(t0 * a.k), ac = (int)((t1 - t0) * a.k);
+  // slice length: a multiple of 64, 16 slices cover the chunk; a slice holds
+  // at most 512 assignments, within one IdBatch, kept in registers for both passes
+  const int len = ((ac + kFusedWaves * 64 - 1) / (kFusedWaves * 64)) * 64;
+  const int s_lo = f0 + (w * len < ac ? w * len : ac);
+  const int s_hi = f0 + ((w + 1) * len < ac ? (w + 1) * len : ac);
+  for (int i = threadIdx.x; i < kFusedWaves * a.E; i += blockDim.x) cnt[i] = 0;
+  IdBatch b;
+  load_batch(a, s_lo, s_hi, lane, &b);
+  __syncthreads();
+  int* mine = cnt + w * a.E;
+  // 1. per-slice histogram; the peer masks are kept for the rank pass
+  uint64_t peers[16];
+  const int n_groups = (s_hi - s_lo + 63) >> 6;
+  int invalid = 0;
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    peers[g] = 0;
+    if (g < n_groups) {  // wave-uniform: slices end on a group boundary except the last
+      const int e = b.e[g];
+      const bool ok = b.active[g] && e >= 0 && e < a.E;
+      invalid += (b.active[g] && !ok) ? 1 : 0;
+      peers[g] = peer_mask(e, ok, a.id_bits);
+      if (ok && (__ffsll((unsigned long long)peers[g]) - 1) == lane)
+        atomicAdd(&mine[e], (int)__popcll(peers[g]));
+    }
+  }
+  __syncthreads();
+  // 2. per expert (thread e): exclusive prefix over slices, then offsets over experts
+  const int e = threadIdx.x;
+  const bool has_e = e < a.E;
+  int count_e = 0;
+  if (has_e)
+    for (int v = 0; v < kFusedWaves; ++v) {
+      const int x = cnt[v * a.E + e];
+      cnt[v * a.E + e] = count_e;
+      count_e += x;
+    }
+  int total;
+  const int off = block_exclusive_scan(has_e ? count_e : 0, &total, lds_waves);
+  if (has_e) {
+    for (int v = 0; v < kFusedWaves; ++v) cnt[v * a.E + e] += off;
+    a.counts[(size_t)c * a.E + e] = count_e;
+    a.offsets[(size_t)c * (a.E + 1) + e] = off;
+    off_lds[e] = off;
+  }
+  if (threadIdx.x == 0) {
+    a.offsets[(size_t)c * (a.E + 1) + a.E] = total;
+    off_lds[a.E] = total;
+  }
+  __syncthreads();
+  const int per = a.E / a.G;
+  for (int g = threadIdx.x; g < a.G; g += blockDim.x)
+    a.splits[(size_t)c * a.G + g] = off_lds[(g + 1) * per] - off_lds[g * per];
+  // 3. stable rank within the slice, from the slice's base per expert
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    if (g < n_groups) {
+      const int f = s_lo + g * 64 + lane;
+      const int ee = b.e[g];
+      const bool ok = b.active[g] && ee >= 0 && ee < a.E;
+      const int leader = ok ? __ffsll((unsigned long long)peers[g]) - 1 : lane;
+      int first = 0;
+      if (ok && leader == lane) first = atomicAdd(&mine[ee], (int)__popcll(peers[g]));
+      first = __shfl(first, leader);
+      const int row = ok ? first + __popcll(peers[g] & lt) : -1;
+      if (b.active[g]) a.dst_row[f] = row;
+      if (ok) a.src_row[f0 + row] = f;
+    }
+  }
+  if (a.dev_error && c == 0) {
+    // dropped ids: this chunk's from the histogram pass, the other chunks' read
+    // here, 16 loads in flight per thread
+    const int n_all = a.T * a.k;
+    int s = invalid;
+    for (int i0 = 0; i0 < n_all - ac; i0 += 16 * 1024) {
+      int id[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = i0 + u * 1024 + (int)threadIdx.x;
+        id[u] = i < n_all - ac ? a.idx[ac + i] : 0;  // chunk 0 holds [0, ac)
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += (id[u] < 0 || id[u] >= a.E) ? 1 : 0;
+    }
+    int dropped;
+    (void)block_exclusive_scan(s, &dropped, lds_waves);
+    if (threadIdx.x == 0) *a.dev_error = dropped;
+  }
+  // rows past the chunk's valid rows hold no assignment
+  for (int r = total + threadIdx.x; r < ac; r += blockDim.x) a.src_row[f0 + r] = -1;
+}
+
 int bits_for(int E) {
   int b = 0;
   while ((1 << b) < E) ++b;
@@ -297,6 +415,11 @@ hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts
   a.spc = p.segs_per_chunk;
   a.seg = p.seg;
   a.id_bits = bits_for(s.E);
+  if (s.E <= kFusedMaxE && (int64_t)s.Tc * s.k <= kFusedMaxIds &&
+      (int64_t)s.T * s.k <= kFusedMaxAll) {
+    hipLaunchKernelGGL(meta_fused, dim3((unsigned)s.N), dim3(1024), 0, st, a);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)s.E * sizeof(int);
   hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
   hipLaunchKernelGGL(meta_scan, dim3((unsigned)s.N), dim3(1024), 0, st, a);
