@@ -127,6 +127,34 @@ def test_route_meta_edge_cases(T, k, E, G, N, bad):
     _check_meta(idx.astype(np.int32), E, G, N, T, k)
 
 
+def _random_meta_shapes(n, seed):
+    """Seeded shapes spread over both metadata paths: chunk sizes around the
+    one-launch limit (8192 assignments per chunk, 65536 in all), E up to 1024
+    with G dividing E, empty and ragged chunks, dropped ids."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 37, 64, 96, 128, 256, 500, 512, 513, 1024]))
+        G = int(rng.choice([g for g in (1, 2, 3, 4, 8, 16, 27) if E % g == 0]))
+        k = int(rng.choice([1, 2, 3, 4, 6, 8, 13]))
+        N = int(rng.choice([1, 2, 3, 4, 5, 8, 9]))
+        per_chunk = int(rng.choice([1, 100, 4000, 8192, 8193, 12000]))
+        T = max(0, min(per_chunk * N // k + int(rng.integers(-3, 4)), 70000 // k))
+        bad = float(rng.choice([0.0, 0.0, 0.01, 0.3]))
+        out.append((T, k, E, G, N, bad))
+    return out
+
+
+@pytest.mark.parametrize("T,k,E,G,N,bad", _random_meta_shapes(24, 2024))
+def test_route_meta_random_shapes(T, k, E, G, N, bad):
+    rng = np.random.default_rng(T * 31 + k * 7 + E + N)
+    idx = rng.integers(0, E, size=(T, k))
+    if bad and T:
+        m = rng.random((T, k)) < bad
+        idx[m] = rng.choice([-1, E, 1 << 20], size=int(m.sum()))
+    _check_meta(idx.astype(np.int32), E, G, N, T, k)
+
+
 # --------------------------------------------------------------------- a2 permute
 @pytest.mark.parametrize("name,N", [("tiny_f32", 1), ("bf16_e64_zipf", 2), ("dsv3_e256", 1),
                                     ("packed16k_e128", 4), ("t3_n4", 4)])
