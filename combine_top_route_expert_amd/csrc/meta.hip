@@ -10,18 +10,23 @@
 // Three launches, deterministic (LDS atomics only add counts, whose sum does
 // not depend on order):
 //  1. meta_hist : one wave per segment of kMetaSeg assignments (segments never
-//     straddle a chunk).  Lanes with equal expert id find each other with one
-//     ballot per id bit; the lowest such lane adds the group's popcount to the
-//     wave's LDS counter.  Writes seg_counts[seg][E] and the dropped-id count.
+//     straddle a chunk).  Every lane adds 1 to its expert's LDS counter.
+//     Writes seg_counts[seg][E] and the dropped-id count.
 //  2. meta_scan : one workgroup per chunk.  Per expert, an exclusive prefix
 //     over the chunk's segments (in place), then a block-wide exclusive scan
 //     over experts gives offsets; seg_counts becomes each segment's first row
 //     per expert.  Also counts, group splits, the -1 tail of src_row, and (in
 //     workgroup 0) dev_error.
-//  3. meta_rank : one wave per segment again.  rank = popcount(peers below me)
-//     plus the segment's running base per expert gives dst_row[f] and
-//     src_row[chunk_start + row] = f.  Lanes are walked in ascending f, so the
-//     permutation is stable.
+//  3. meta_rank : one wave per segment again.  Lanes with equal expert id find
+//     each other with one ballot per id bit (peer_mask); rank = popcount(peers
+//     below me) plus the segment's running base per expert gives dst_row[f]
+//     and src_row[chunk_start + row] = f.  Lanes are walked in ascending f, so
+//     the permutation is stable.
+//
+// Chunks of at most kHistScanMaxIds assignments (at most kFusedMaxAll in all)
+// fold steps 1 and 2 into one launch, meta_hist_scan: one 1024-thread
+// workgroup per chunk counts every segment of the chunk into the staged LDS
+// block and scans it in place; meta_rank, spread over the chip, follows.
 //
 // Chunks of at most kFusedMaxIds assignments (E <= kFusedMaxE, at most
 // kFusedMaxAll assignments in all) take one launch instead: meta_fused runs
@@ -114,10 +119,7 @@ __global__ void __launch_bounds__(64) meta_hist(MetaArgs a) {
       const int e = b.e[g];
       const bool ok = b.active[g] && e >= 0 && e < a.E;
       invalid += (b.active[g] && !ok) ? 1 : 0;
-      const uint64_t peers = peer_mask(e, ok, a.id_bits);
-      // one add per distinct expert of the group; the total does not depend on order
-      if (ok && (__ffsll((unsigned long long)peers) - 1) == lane)
-        atomicAdd(&cnt[e], (int)__popcll(peers));
+      if (ok) atomicAdd(&cnt[e], 1);  // counts only: the sum does not depend on order
     }
   }
   __syncthreads();
@@ -154,11 +156,9 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds_waves) {
   return r;
 }
 
-__global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
-  __shared__ int stage[kScanStage];
-  __shared__ int lds_waves[48];
-  __shared__ int off_lds[kMaxExperts + 1];
-  const int c = blockIdx.x;  // one workgroup per chunk
+// Scan of chunk c's [segments][E] counts, staged in LDS: counts, offsets,
+// group splits, the segment bases (to seg_counts) and the -1 tail of src_row.
+__device__ void scan_chunk(const MetaArgs& a, int c, int* stage, int* lds_waves, int* off_lds) {
   // P consecutive lanes per expert (P a power of two, P * E <= 1024) share the
   // prefix over the chunk's segments: each sums a contiguous run of segments,
   // the P partial sums are scanned with lane shuffles, then each lane writes
@@ -167,11 +167,8 @@ __global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
   while (P > 1 && P * a.E > (int)blockDim.x) P >>= 1;
   const int e = threadIdx.x / P, part = threadIdx.x % P;
   const bool has_e = e < a.E;
-  const size_t seg0 = (size_t)c * a.spc;
   const int n_stage = a.spc * a.E;  // <= kScanStage by the plan
-  int32_t* blk = a.seg_counts + seg0 * a.E;
-  for (int i = threadIdx.x; i < n_stage; i += blockDim.x) stage[i] = blk[i];
-  __syncthreads();
+  int32_t* blk = a.seg_counts + (size_t)c * a.spc * a.E;
   const int len = (a.spc + P - 1) / P;
   const int j0 = part * len < a.spc ? part * len : a.spc;
   const int j1 = j0 + len < a.spc ? j0 + len : a.spc;
@@ -215,10 +212,85 @@ __global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
   if (t1 > a.T) t1 = a.T;
   const long long f0 = t0 * a.k, ac = (t1 - t0) * a.k;
   for (long long r = total + threadIdx.x; r < ac; r += blockDim.x) a.src_row[f0 + r] = -1;
+}
+
+__global__ void __launch_bounds__(1024) meta_scan(MetaArgs a) {
+  __shared__ int stage[kScanStage];
+  __shared__ int lds_waves[48];
+  __shared__ int off_lds[kMaxExperts + 1];
+  const int c = blockIdx.x;  // one workgroup per chunk
+  const int n_stage = a.spc * a.E;
+  const int32_t* blk = a.seg_counts + (size_t)c * a.spc * a.E;
+  for (int i = threadIdx.x; i < n_stage; i += blockDim.x) stage[i] = blk[i];
+  __syncthreads();
+  scan_chunk(a, c, stage, lds_waves, off_lds);
   if (a.dev_error && c == 0) {
     int s = 0;
     const long long nseg = (long long)a.N * a.spc;
     for (long long i = threadIdx.x; i < nseg; i += blockDim.x) s += a.seg_invalid[i];
+    int dropped;
+    (void)block_exclusive_scan(s, &dropped, lds_waves);
+    if (threadIdx.x == 0) *a.dev_error = dropped;
+  }
+}
+
+// Dropped ids among idx[lo, hi), summed over this thread's share (1024
+// threads, 16 loads in flight per thread).
+__device__ int count_dropped(const MetaArgs& a, int lo, int hi) {
+  int s = 0;
+  for (int i0 = lo; i0 < hi; i0 += 16 * 1024) {
+    int id[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * 1024 + (int)threadIdx.x;
+      id[u] = i < hi ? a.idx[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += (id[u] < 0 || id[u] >= a.E) ? 1 : 0;
+  }
+  return s;
+}
+
+// Histogram and scan of one chunk in one workgroup (chunks of up to
+// kHistScanMaxIds assignments); meta_rank follows.  Wave w takes a contiguous
+// run of the chunk's segments; a 64-id group never straddles two segments
+// (segments are multiples of 256 ids), so each group adds to one row of the
+// staged [segments][E] block.  Workgroup 0 adds the other chunks' dropped ids
+// to its own.
+__global__ void __launch_bounds__(1024) meta_hist_scan(MetaArgs a) {
+  __shared__ int stage[kScanStage];
+  __shared__ int lds_waves[48];
+  __shared__ int off_lds[kMaxExperts + 1];
+  const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n_stage = a.spc * a.E;
+  for (int i = threadIdx.x; i < n_stage; i += blockDim.x) stage[i] = 0;
+  __syncthreads();
+  long long t0 = (long long)c * a.Tc, t1 = (long long)(c + 1) * a.Tc;
+  if (t0 > a.T) t0 = a.T;
+  if (t1 > a.T) t1 = a.T;
+  const int cf0 = (int)(t0 * a.k), ac = (int)((t1 - t0) * a.k);
+  const int spw = (a.spc + 15) / 16;  // segments per wave
+  const long long lo_l = (long long)w * spw * a.seg, hi_l = lo_l + (long long)spw * a.seg;
+  const int f_lo = cf0 + (int)(lo_l < ac ? lo_l : ac);
+  const int f_hi = cf0 + (int)(hi_l < ac ? hi_l : ac);
+  int invalid = 0;
+  for (int b0 = f_lo; b0 < f_hi; b0 += 1024) {
+    IdBatch b;
+    load_batch(a, b0, f_hi, lane, &b);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      if (b0 + g * 64 >= f_hi) break;
+      int* row = stage + ((b0 + g * 64 - cf0) / a.seg) * a.E;
+      const int e = b.e[g];
+      const bool ok = b.active[g] && e >= 0 && e < a.E;
+      invalid += (b.active[g] && !ok) ? 1 : 0;
+      if (ok) atomicAdd(&row[e], 1);  // counts only: the sum does not depend on order
+    }
+  }
+  __syncthreads();
+  scan_chunk(a, c, stage, lds_waves, off_lds);
+  if (a.dev_error && c == 0) {
+    const int s = invalid + count_dropped(a, ac, a.T * a.k);  // chunk 0 holds [0, ac)
     int dropped;
     (void)block_exclusive_scan(s, &dropped, lds_waves);
     if (threadIdx.x == 0) *a.dev_error = dropped;
@@ -263,6 +335,7 @@ constexpr int kFusedWaves = 16;
 constexpr int kFusedMaxE = 512;       // LDS: kFusedWaves * E counters
 constexpr int kFusedMaxIds = 8192;    // assignments of one chunk
 constexpr int64_t kFusedMaxAll = 65536;  // all chunks (workgroup 0 counts dropped ids)
+constexpr int kHistScanMaxIds = 32768;   // assignments of one chunk, meta_hist_scan
 
 __global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
   __shared__ int cnt[kFusedWaves * kFusedMaxE];  // [slice][E]
@@ -344,20 +417,8 @@ __global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
     }
   }
   if (a.dev_error && c == 0) {
-    // dropped ids: this chunk's from the histogram pass, the other chunks' read
-    // here, 16 loads in flight per thread
-    const int n_all = a.T * a.k;
-    int s = invalid;
-    for (int i0 = 0; i0 < n_all - ac; i0 += 16 * 1024) {
-      int id[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int i = i0 + u * 1024 + (int)threadIdx.x;
-        id[u] = i < n_all - ac ? a.idx[ac + i] : 0;  // chunk 0 holds [0, ac)
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) s += (id[u] < 0 || id[u] >= a.E) ? 1 : 0;
-    }
+    // dropped ids: this chunk's from the histogram pass, the other chunks' read here
+    const int s = invalid + count_dropped(a, ac, a.T * a.k);  // chunk 0 holds [0, ac)
     int dropped;
     (void)block_exclusive_scan(s, &dropped, lds_waves);
     if (threadIdx.x == 0) *a.dev_error = dropped;
@@ -421,6 +482,11 @@ hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts
     return hipGetLastError();
   }
   const size_t lds = (size_t)s.E * sizeof(int);
+  if ((int64_t)s.Tc * s.k <= kHistScanMaxIds && (int64_t)s.T * s.k <= kFusedMaxAll) {
+    hipLaunchKernelGGL(meta_hist_scan, dim3((unsigned)s.N), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
   hipLaunchKernelGGL(meta_scan, dim3((unsigned)s.N), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds, st, a);

@@ -108,15 +108,20 @@ def test_route_meta_bit_exact(name, N, G):
     (300, 64, 1024, 16, 3, 0.02),  # largest E with dropped ids and three chunks
     (5000, 8, 512, 8, 2, 0.03),
     (16384, 8, 96, 3, 2, 0.01),    # E not a power of two, 65536 assignments per chunk
-    # either side of the one-launch (fused) limits: 8192 assignments per chunk,
-    # 65536 in all, E = 512
-    (1024, 8, 64, 1, 1, 0.02),     # 8192 in one chunk: fused
-    (1025, 8, 64, 1, 1, 0.02),     # 8200: three launches
-    (8192, 8, 512, 8, 8, 0.01),    # 8 x 8192 = 65536, E = 512: fused
-    (8193, 8, 512, 8, 8, 0.01),    # 8200 per chunk: three launches
+    # either side of the metadata paths' limits: one launch up to 8192
+    # assignments per chunk (E <= 512), two up to 32768, both only up to 65536
+    # assignments in all, three otherwise
+    (1024, 8, 64, 1, 1, 0.02),     # 8192 in one chunk: one launch
+    (1025, 8, 64, 1, 1, 0.02),     # 8200: two launches
+    (8192, 8, 512, 8, 8, 0.01),    # 8 x 8192 = 65536, E = 512: one launch
+    (8193, 8, 512, 8, 8, 0.01),    # 65544 in all: three launches
     (8200, 8, 256, 16, 9, 0.01),   # 65600 in all: three launches
-    (900, 8, 513, 27, 1, 0.01),    # E = 513: three launches
-    (1000, 13, 37, 1, 3, 0.05),    # fused, ragged slices and chunks
+    (900, 8, 513, 27, 1, 0.01),    # E = 513: two launches
+    (1000, 13, 37, 1, 3, 0.05),    # one launch, ragged slices and chunks
+    (4096, 8, 256, 16, 2, 0.01),   # 2 x 16384: two launches
+    (4096, 16, 1024, 16, 2, 0.01),  # 2 x 32768, E = 1024 (segments of 2048): two launches
+    (4097, 16, 1024, 16, 2, 0.0),  # 32784 per chunk, 65552 in all: three launches
+    (3000, 7, 96, 3, 1, 0.2),      # 21000 in one chunk, many dropped: two launches
 ])
 def test_route_meta_edge_cases(T, k, E, G, N, bad):
     rng = np.random.default_rng(T + k + E)
