@@ -392,7 +392,7 @@ def main():
     tok0 = chunk_rows[0] // cfg.k  # tokens of chunk 0
     dn_bytes = rows0 * I * s + e_act0 * H * I * s + rows0 * H * s
     per_kernel = {
-        "route_meta": (12 * cfg.T * cfg.k, 0.0, "all chunks: ids read twice, src_row and dst_row"),
+        "route_meta": (12 * cfg.T * cfg.k, 0.0, "all chunks: ids read once, src_row and dst_row written"),
         "permute": (tok0 * H * s + chunk_rows[0] * H * s + 4 * chunk_rows[0], 0.0,
                     "chunk 0 (per-chunk schedule; the pair-fused layer gathers in gate_up)"),
         "gate_up": (gu_bytes, gu_flops, "chunks 0-1, rows gathered from hidden_states"),
