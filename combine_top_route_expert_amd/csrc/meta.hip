@@ -438,8 +438,8 @@ int bits_for(int E) {
 MetaPlan meta_plan(const Shape& s) {
   MetaPlan p{};
   const int64_t ac = (int64_t)s.Tc * s.k;
-  // segment = a multiple of 1024 assignments, large enough that one chunk's
-  // [segments][E] counts fit the scan kernel's LDS block
+  // segment = a multiple of kMetaSeg (256) assignments, large enough that one
+  // chunk's [segments][E] counts fit the scan kernel's LDS block
   int64_t seg = kMetaSeg;
   while (((ac + seg - 1) / seg) * s.E > kScanStage) seg += kMetaSeg;
   p.seg = (int)seg;
