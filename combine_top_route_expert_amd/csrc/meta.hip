@@ -18,10 +18,10 @@
 //     per expert.  Also counts, group splits, the -1 tail of src_row, and (in
 //     workgroup 0) dev_error.
 //  3. meta_rank : one wave per segment again.  Lanes with equal expert id find
-//     each other with one ballot per id bit (peer_mask); rank = popcount(peers
-//     below me) plus the segment's running base per expert gives dst_row[f]
-//     and src_row[chunk_start + row] = f.  Lanes are walked in ascending f, so
-//     the permutation is stable.
+//     each other through one LDS word per expert (peer_mask: an OR of lane
+//     bits); rank = popcount(peers below me) plus the segment's running base
+//     per expert gives dst_row[f] and src_row[chunk_start + row] = f.  Lanes
+//     are walked in ascending f, so the permutation is stable.
 //
 // Chunks of at most kHistScanMaxIds assignments (at most kFusedMaxAll in all)
 // fold steps 1 and 2 into one launch, meta_hist_scan: one 1024-thread
@@ -33,11 +33,11 @@
 // the same three steps in one 1024-thread workgroup per chunk.  Wave w owns
 // the w-th of 16 contiguous slices of the chunk (at most 512 assignments, held
 // in registers with their peer masks from the histogram pass to the rank pass)
-// and keeps its per-expert counts in row w of LDS, so the prefix over slices
-// takes the place of the prefix over segments and no step waits on another
-// launch.  Workgroup 0 also counts the dropped ids of every chunk.  Chunks this
-// small are latency-bound: the two extra launches and the round trip of the
-// segment counts through memory cost more than the work.
+// and keeps its per-expert counts and peer words in row w of LDS, so the
+// prefix over slices takes the place of the prefix over segments and no step
+// waits on another launch.  Workgroup 0 also counts the dropped ids of every
+// chunk.  Chunks this small are latency-bound: the two extra launches and the
+// round trip of the segment counts through memory cost more than the work.
 #include "moe_internal.h"
 
 namespace moe {
@@ -54,7 +54,7 @@ struct MetaArgs {
   int32_t* src_row;
   int32_t* dst_row;
   int32_t* dev_error;
-  int T, k, E, G, N, Tc, spc, seg, id_bits;
+  int T, k, E, G, N, Tc, spc, seg;
 };
 
 // Segment `seg` -> its chunk and flat range [f_lo, f_hi).
@@ -74,15 +74,19 @@ __device__ __forceinline__ void seg_range(const MetaArgs& a, int seg, int* chunk
   *chunk_f0 = (int)(t0 * a.k);
 }
 
-// Mask of the lanes whose (valid) expert id equals this lane's.
-__device__ __forceinline__ uint64_t peer_mask(int e, bool ok, int id_bits) {
-  uint64_t m = __ballot(ok);
-  for (int b = 0; b < id_bits; ++b) {
-    bool bit = (e >> b) & 1;
-    uint64_t vb = __ballot(bit);
-    m &= bit ? vb : ~vb;
-  }
-  return m;
+// Mask of the lanes of this wave whose (valid) expert id equals this lane's,
+// through one LDS word per expert: every valid lane ORs its bit into word[e]
+// and reads the word back.  One wave's LDS operations complete in program
+// order, so the read sees every OR of the instruction before it, and the
+// result of an OR does not depend on the order in which the lanes are served.
+// The words start at zero; the caller's group leader clears word[e] after the
+// read (a later instruction, so every peer has read it by then).  Lanes that
+// share a word are served one at a time, so a skewed group costs more than a
+// spread one; an earlier form that took one ballot per id bit cost more on
+// every workload but the most skewed.
+__device__ __forceinline__ uint64_t peer_mask(unsigned long long* word, int e, bool ok) {
+  if (ok) atomicOr(&word[e], 1ull << __lane_id());
+  return ok ? (uint64_t)word[e] : 0;
 }
 
 // Ids of one 1024-assignment batch, 16 per lane, loaded together so their
@@ -298,13 +302,18 @@ __global__ void __launch_bounds__(1024) meta_hist_scan(MetaArgs a) {
 }
 
 __global__ void __launch_bounds__(64) meta_rank(MetaArgs a) {
-  extern __shared__ int base[];
+  extern __shared__ unsigned long long dyn[];  // [E] peer words, then [E] bases
+  unsigned long long* word = dyn;
+  int* base = (int*)(dyn + a.E);
   const int lane = threadIdx.x;
   int c, f_lo, f_hi, cf0;
   seg_range(a, blockIdx.x, &c, &f_lo, &f_hi, &cf0);
   (void)c;
   const int32_t* sb = a.seg_counts + (size_t)blockIdx.x * a.E;
-  for (int e = lane; e < a.E; e += 64) base[e] = sb[e];
+  for (int e = lane; e < a.E; e += 64) {
+    base[e] = sb[e];
+    word[e] = 0;
+  }
   __syncthreads();
   const uint64_t lt = lanemask_lt();
   for (int b0 = f_lo; b0 < f_hi; b0 += 1024) {
@@ -316,13 +325,16 @@ __global__ void __launch_bounds__(64) meta_rank(MetaArgs a) {
       const int f = b0 + g * 64 + lane;
       const int e = b.e[g];
       const bool ok = b.active[g] && e >= 0 && e < a.E;
-      const uint64_t peers = peer_mask(e, ok, a.id_bits);
+      const uint64_t peers = peer_mask(word, e, ok);
       const int leader = ok ? __ffsll((unsigned long long)peers) - 1 : lane;
       // the leader takes the group's rows from its expert's running base (groups
       // of earlier lanes and earlier iterations come first: program order of
       // one wave); every peer adds its rank among the group's lanes
       int first = 0;
-      if (ok && leader == lane) first = atomicAdd(&base[e], (int)__popcll(peers));
+      if (ok && leader == lane) {
+        first = atomicAdd(&base[e], (int)__popcll(peers));
+        word[e] = 0;
+      }
       first = __shfl(first, leader);
       const int row = ok ? first + __popcll(peers & lt) : -1;
       if (b.active[g]) a.dst_row[f] = row;
@@ -339,6 +351,7 @@ constexpr int kHistScanMaxIds = 32768;   // assignments of one chunk, meta_hist_
 
 __global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
   __shared__ int cnt[kFusedWaves * kFusedMaxE];  // [slice][E]
+  __shared__ unsigned long long pw[kFusedWaves * kFusedMaxE];  // [slice][E] peer words
   __shared__ int off_lds[kFusedMaxE + 1];
   __shared__ int lds_waves[48];
   const int c = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -351,15 +364,20 @@ __global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
   const int len = ((ac + kFusedWaves * 64 - 1) / (kFusedWaves * 64)) * 64;
   const int s_lo = f0 + (w * len < ac ? w * len : ac);
   const int s_hi = f0 + ((w + 1) * len < ac ? (w + 1) * len : ac);
-  for (int i = threadIdx.x; i < kFusedWaves * a.E; i += blockDim.x) cnt[i] = 0;
+  for (int i = threadIdx.x; i < kFusedWaves * a.E; i += blockDim.x) {
+    cnt[i] = 0;
+    pw[i] = 0;
+  }
   IdBatch b;
   load_batch(a, s_lo, s_hi, lane, &b);
   __syncthreads();
   int* mine = cnt + w * a.E;
-  // 1. per-slice histogram; the peer masks are kept for the rank pass
-  uint64_t peers[16];
+  unsigned long long* words = pw + w * a.E;
+  // 1. per-slice histogram: each group's peer masks, kept for the rank pass,
+  // and one add of the group's popcount per expert by its lowest lane
   const int n_groups = (s_hi - s_lo + 63) >> 6;
   int invalid = 0;
+  uint64_t peers[16];
 #pragma unroll
   for (int g = 0; g < 16; ++g) {
     peers[g] = 0;
@@ -367,9 +385,11 @@ __global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
       const int e = b.e[g];
       const bool ok = b.active[g] && e >= 0 && e < a.E;
       invalid += (b.active[g] && !ok) ? 1 : 0;
-      peers[g] = peer_mask(e, ok, a.id_bits);
-      if (ok && (__ffsll((unsigned long long)peers[g]) - 1) == lane)
+      peers[g] = peer_mask(words, e, ok);
+      if (ok && (__ffsll((unsigned long long)peers[g]) - 1) == lane) {
         atomicAdd(&mine[e], (int)__popcll(peers[g]));
+        words[e] = 0;
+      }
     }
   }
   __syncthreads();
@@ -427,12 +447,6 @@ __global__ void __launch_bounds__(1024) meta_fused(MetaArgs a) {
   for (int r = total + threadIdx.x; r < ac; r += blockDim.x) a.src_row[f0 + r] = -1;
 }
 
-int bits_for(int E) {
-  int b = 0;
-  while ((1 << b) < E) ++b;
-  return b;
-}
-
 }  // namespace
 
 MetaPlan meta_plan(const Shape& s) {
@@ -475,21 +489,21 @@ hipError_t launch_route_meta(const Shape& s, const int32_t* idx, int32_t* counts
   a.Tc = s.Tc;
   a.spc = p.segs_per_chunk;
   a.seg = p.seg;
-  a.id_bits = bits_for(s.E);
   if (s.E <= kFusedMaxE && (int64_t)s.Tc * s.k <= kFusedMaxIds &&
       (int64_t)s.T * s.k <= kFusedMaxAll) {
     hipLaunchKernelGGL(meta_fused, dim3((unsigned)s.N), dim3(1024), 0, st, a);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)s.E * sizeof(int);
+  const size_t lds_rank = (size_t)s.E * (sizeof(unsigned long long) + sizeof(int));
   if ((int64_t)s.Tc * s.k <= kHistScanMaxIds && (int64_t)s.T * s.k <= kFusedMaxAll) {
     hipLaunchKernelGGL(meta_hist_scan, dim3((unsigned)s.N), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
+    hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds_rank, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
+  hipLaunchKernelGGL(meta_hist, dim3((unsigned)p.nseg), dim3(64), (size_t)s.E * sizeof(int), st,
+                     a);
   hipLaunchKernelGGL(meta_scan, dim3((unsigned)s.N), dim3(1024), 0, st, a);
-  hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds, st, a);
+  hipLaunchKernelGGL(meta_rank, dim3((unsigned)p.nseg), dim3(64), lds_rank, st, a);
   return hipGetLastError();
 }
 
