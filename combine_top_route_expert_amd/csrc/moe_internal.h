@@ -331,10 +331,8 @@ struct MTileMap {
 // more than ceil(total/8) m-tiles and the work is spread evenly.  In which
 // order: the XCD's large and small m-tiles are interleaved evenly, so that
 // MFMA-bound large tiles and weight-streaming small tiles run side by side
-// (small tiles started all together contend for HBM), except that its last
-// ceil(32/n_tiles) m-tiles (about one workgroup per CU) are its smallest ones,
-// which shortens the tail of the launch.  Every m-tile comes with all its
-// n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
+// (small tiles started all together contend for HBM).  Every m-tile comes with
+// all its n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
 // those past their XCD's share exit.
 // xcd_tile_at: the same for position q of XCD x's sequence (a workgroup that
 // takes several tiles walks q, q + G, q + 2G, ... with G its XCD's workgroup
@@ -356,27 +354,19 @@ __device__ __forceinline__ bool xcd_tile_at(const MTileMap& tm, int n_tiles, int
   if (S > D + x) ns += (S - D - x + 7) / 8;
   const int C = nl + ns;
   if (ml >= C) return false;
-  int R = (32 + n_tiles - 1) / n_tiles;  // small m-tiles kept for the end
-  R = R < ns ? R : ns;
-  const int C1 = C - R;                  // positions of the even interleave
-  int j;                                 // this XCD's j-th small m-tile
-  if (ml >= C1) {
-    j = ns - R + (ml - C1);
+  int lb, la;  // large m-tiles before positions ml and ml + 1 of the even interleave
+  if (C < 65536) {  // nl <= C: the products fit 32 bits
+    lb = (int)((unsigned)ml * (unsigned)nl / (unsigned)C);
+    la = (int)((unsigned)(ml + 1) * (unsigned)nl / (unsigned)C);
   } else {
-    int lb, la;  // large m-tiles before positions ml and ml + 1
-    if (C1 < 65536) {  // nl <= C1: the products fit 32 bits
-      lb = (int)((unsigned)ml * (unsigned)nl / (unsigned)C1);
-      la = (int)((unsigned)(ml + 1) * (unsigned)nl / (unsigned)C1);
-    } else {
-      lb = (int)((long long)ml * nl / C1);
-      la = (int)((long long)(ml + 1) * nl / C1);
-    }
-    if (la > lb) {
-      *mt = x * per + lb;
-      return true;
-    }
-    j = ml - lb;
+    lb = (int)((long long)ml * nl / C);
+    la = (int)((long long)(ml + 1) * nl / C);
   }
+  if (la > lb) {
+    *mt = x * per + lb;
+    return true;
+  }
+  const int j = ml - lb;  // this XCD's j-th small m-tile
   const int p = j < deficit ? before + j : D + (j - deficit) * 8 + x;
   *mt = tm.large + p;
   return *mt < tm.total;
