@@ -331,14 +331,16 @@ struct MTileMap {
 // more than ceil(total/8) m-tiles and the work is spread evenly.  In which
 // order: the XCD's large and small m-tiles are interleaved evenly, so that
 // MFMA-bound large tiles and weight-streaming small tiles run side by side
-// (small tiles started all together contend for HBM).  Every m-tile comes with
-// all its n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
+// (small tiles started all together contend for HBM), except that its last
+// `reserve` m-tiles may be kept for its smallest ones, to shorten the tail of
+// the launch (xcd_tile: ceil(32/n_tiles), about one workgroup per CU; the
+// forward grouped GEMM passes 0).  Every m-tile comes with all its n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
 // those past their XCD's share exit.
 // xcd_tile_at: the same for position q of XCD x's sequence (a workgroup that
 // takes several tiles walks q, q + G, q + 2G, ... with G its XCD's workgroup
 // count); false once q is past the XCD's tiles.
 __device__ __forceinline__ bool xcd_tile_at(const MTileMap& tm, int n_tiles, int x, int q,
-                                            int* mt, int* nt) {
+                                            int reserve, int* mt, int* nt) {
   const int ml = q / n_tiles;
   *nt = q - ml * n_tiles;
   const int per = (tm.large + 7) >> 3;
@@ -354,26 +356,34 @@ __device__ __forceinline__ bool xcd_tile_at(const MTileMap& tm, int n_tiles, int
   if (S > D + x) ns += (S - D - x + 7) / 8;
   const int C = nl + ns;
   if (ml >= C) return false;
-  int lb, la;  // large m-tiles before positions ml and ml + 1 of the even interleave
-  if (C < 65536) {  // nl <= C: the products fit 32 bits
-    lb = (int)((unsigned)ml * (unsigned)nl / (unsigned)C);
-    la = (int)((unsigned)(ml + 1) * (unsigned)nl / (unsigned)C);
+  const int R = reserve < ns ? reserve : ns;  // small m-tiles kept for the end
+  const int C1 = C - R;                       // positions of the even interleave
+  int j;                                      // this XCD's j-th small m-tile
+  if (ml >= C1) {
+    j = ns - R + (ml - C1);
   } else {
-    lb = (int)((long long)ml * nl / C);
-    la = (int)((long long)(ml + 1) * nl / C);
+    int lb, la;  // large m-tiles before positions ml and ml + 1
+    if (C1 < 65536) {  // nl <= C1: the products fit 32 bits
+      lb = (int)((unsigned)ml * (unsigned)nl / (unsigned)C1);
+      la = (int)((unsigned)(ml + 1) * (unsigned)nl / (unsigned)C1);
+    } else {
+      lb = (int)((long long)ml * nl / C1);
+      la = (int)((long long)(ml + 1) * nl / C1);
+    }
+    if (la > lb) {
+      *mt = x * per + lb;
+      return true;
+    }
+    j = ml - lb;
   }
-  if (la > lb) {
-    *mt = x * per + lb;
-    return true;
-  }
-  const int j = ml - lb;  // this XCD's j-th small m-tile
   const int p = j < deficit ? before + j : D + (j - deficit) * 8 + x;
   *mt = tm.large + p;
   return *mt < tm.total;
 }
 
 __device__ __forceinline__ bool xcd_tile(const MTileMap& tm, int n_tiles, int* mt, int* nt) {
-  return xcd_tile_at(tm, n_tiles, blockIdx.x & 7, blockIdx.x >> 3, mt, nt);
+  return xcd_tile_at(tm, n_tiles, blockIdx.x & 7, blockIdx.x >> 3, (32 + n_tiles - 1) / n_tiles,
+                     mt, nt);
 }
 
 // Round-robin variant: XCD x takes m-tiles x, x + 8, x + 16, ... (each with all
