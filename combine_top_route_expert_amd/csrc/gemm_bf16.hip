@@ -491,7 +491,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     // which mixes weight-streaming and MFMA-bound tiles on a CU (measured faster)
     tm.build(a.off0, a.off1, a.E, BM, BM >= 128 ? BM : 1);
     int mt, nt;
-    if (!xcd_tile_at(tm, a.n_tiles, xcd, q, 0, &mt, &nt)) break;
+    if (!xcd_tile_at(tm, a.n_tiles, xcd, q, (32 + a.n_tiles - 1) / a.n_tiles, &mt, &nt)) break;
     const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
     Loader ld;
     ld.init(a, tr, nt, lane, wave);

@@ -332,9 +332,9 @@ struct MTileMap {
 // order: the XCD's large and small m-tiles are interleaved evenly, so that
 // MFMA-bound large tiles and weight-streaming small tiles run side by side
 // (small tiles started all together contend for HBM), except that its last
-// `reserve` m-tiles may be kept for its smallest ones, to shorten the tail of
-// the launch (xcd_tile: ceil(32/n_tiles), about one workgroup per CU; the
-// forward grouped GEMM passes 0).  Every m-tile comes with all its n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
+// `reserve` m-tiles are kept for its smallest ones, to shorten the tail of the
+// launch (every caller passes ceil(32/n_tiles), about one workgroup per CU).
+// Every m-tile comes with all its n-tiles.  The grid has 8 * ceil(bound/8) * n_tiles workgroups (xcd_grid);
 // those past their XCD's share exit.
 // xcd_tile_at: the same for position q of XCD x's sequence (a workgroup that
 // takes several tiles walks q, q + G, q + 2G, ... with G its XCD's workgroup
