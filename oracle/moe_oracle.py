@@ -55,6 +55,7 @@ __all__ = [
     "chunk_bounds", "resolve_num_chunks", "w_pair_rows", "route_meta", "permute",
     "silu", "expert_act", "expert_ffn", "unpermute_combine", "moe_forward", "moe_tokens",
     "silu_grad", "moe_backward", "moe_tokens_backward", "expert_weight_grads",
+    "row_rel_err",
 ]
 
 
@@ -389,10 +390,22 @@ def expert_weight_grads(e: int, hidden: np.ndarray, top_k_index: np.ndarray,
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
-    """max over rows t of ||got_t - ref_t||_inf / max(||ref_t||_inf, 1e-30)."""
+    """The comparison metric for floating-point outputs (the pages give a
+    tolerance's size but not its norm; the reading taken is row-wise):
+    max over rows t of ||got_t - ref_t||_inf / max(||ref_t||_inf, 1e-30).
+
+    Both arrays must be 2-D with the same shape (no broadcasting: a wrong row
+    count is an error, not a comparison of other rows).  A NaN or infinity in
+    either array gives +inf, so no tolerance accepts it.  No rows gives 0."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    if got.size == 0:
+    if got.ndim != 2 or got.shape != ref.shape:
+        raise ValueError(f"row_rel_err: shapes {got.shape} and {ref.shape} differ or are not 2-D")
+    if got.shape[0] == 0:
+        return 0.0
+    if not (np.isfinite(got).all() and np.isfinite(ref).all()):
+        return float("inf")
+    if got.shape[1] == 0:
         return 0.0
     num = np.abs(got - ref).max(axis=1)
     den = np.maximum(np.abs(ref).max(axis=1), 1e-30)

@@ -380,10 +380,58 @@ def check_backward_views_and_chunking():
             assert np.allclose(b["grad_wd"][e], ref["grad_wd"][e], rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- parity metric
+def check_row_rel_err():
+    """The comparison metric, on hand-computed 3 x 4 cases: the row-wise
+    inf-norm relative error max_t max_h |g - r| / max(max_h |r|, 1e-30) (the
+    reading taken for the unnamed norm of the tolerances).  The cases are built
+    so that the whole-array ratio, the elementwise ratio and a signed
+    difference all give other values."""
+    ref = np.array([[10.0, 0.01, 0.0, 0.0],
+                    [0.0, 1.0, 0.0, 0.0],
+                    [0.0, 0.0, 0.0, 0.0]])
+    got = np.array([[10.5, 0.02, 0.0, 0.0],   # row error 0.5 / 10 = 0.05 (elementwise: 1.0)
+                    [0.0, 1.25, 0.0, 0.0],    # row error 0.25 / 1 = 0.25
+                    [0.0, 0.0, 0.0, 0.0]])    # zero row, exact: 0
+    # by hand: max(0.05, 0.25, 0) = 0.25; whole-array ratio would be 0.5 / 10 = 0.05
+    assert om.row_rel_err(got, ref) == 0.25
+    # the metric is symmetric in the row it measures, not in its arguments:
+    # swapping them divides by the other row's norm (0.25 / 1.25 = 0.2 for row 1)
+    assert om.row_rel_err(ref, got) == max(0.5 / 10.5, 0.25 / 1.25)
+    # a sign flip: |(-1) - 1| / 1 = 2 (a signed difference would give 0 there)
+    flip = got.copy()
+    flip[1, 1] = -1.0
+    assert om.row_rel_err(flip, ref) == 2.0
+    # a below-reference error only: |0.75 - 1| / 1 = 0.25 (a signed max would miss it)
+    low = ref.copy()
+    low[1, 1] = 0.75
+    assert om.row_rel_err(low, ref) == 0.25
+    # an all-zero reference row is measured against the floor 1e-30
+    tiny = ref.copy()
+    tiny[2, 2] = 2e-31
+    assert math.isclose(om.row_rel_err(tiny, ref), 0.2, rel_tol=1e-12)
+    # identical arrays and no rows give 0
+    assert om.row_rel_err(ref, ref) == 0.0
+    assert om.row_rel_err(np.zeros((0, 4)), np.zeros((0, 4))) == 0.0
+    # a NaN or infinity fails every tolerance
+    bad = got.copy()
+    bad[2, 3] = np.nan
+    assert not om.row_rel_err(bad, ref) <= 1e30
+    bad[2, 3] = np.inf
+    assert not om.row_rel_err(bad, ref) <= 1e30
+    # one row against three is an error, not a broadcast comparison
+    for g, r in ((got[:1], ref), (got, ref[:, :3]), (got[0], ref[0])):
+        try:
+            om.row_rel_err(g, r)
+        except ValueError:
+            continue
+        raise AssertionError(f"row_rel_err accepted shapes {np.shape(g)} and {np.shape(r)}")
+
+
 ALL_CHECKS = [
     check_chunk_bounds, check_resolve_num_chunks, check_w_pair, check_route_meta_library,
     check_route_meta_bruteforce, check_silu, check_ffn_closed_form, check_ffn_bruteforce,
     check_identity_k1, check_identical_experts_dense, check_weights_linear_and_dropped_slots,
     check_plain_definition_vs_chunked, check_silu_grad, check_backward_finite_differences,
-    check_backward_views_and_chunking,
+    check_backward_views_and_chunking, check_row_rel_err,
 ]

@@ -10,6 +10,7 @@ import oracle_checks
 _orig_route_meta = om.route_meta
 _orig_expert_ffn = om.expert_ffn
 _orig_moe_backward = om.moe_backward
+_orig_row_rel_err = om.row_rel_err
 
 
 def _silu_as_sigmoid(z):
@@ -108,6 +109,38 @@ def _backward_grad_w_slots_reversed(*a, **kw):
     return b
 
 
+def _row_rel_err_whole_array(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if got.size == 0:
+        return 0.0
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def _row_rel_err_signed(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if got.size == 0:
+        return 0.0
+    num = (got - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((num / den).max())
+
+
+def _row_rel_err_elementwise(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if got.size == 0:
+        return 0.0
+    return float((np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)).max())
+
+
+def _row_rel_err_broadcasts(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if got.size == 0:
+        return 0.0
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return float(np.max(num / den))
+
+
 MUTANTS = {
     "silu_grad_no_z_term": ("silu_grad", _silu_grad_no_z_term),
     "backward_unweighted": ("moe_backward", _backward_unweighted),
@@ -123,6 +156,10 @@ MUTANTS = {
     "chunk_bounds_floor": ("chunk_bounds", _chunk_bounds_floor),
     "resolve_chunk_size_wins": ("resolve_num_chunks", _resolve_size_wins),
     "w_pair_no_min": ("w_pair_rows", _w_pair_no_min),
+    "row_rel_err_whole_array": ("row_rel_err", _row_rel_err_whole_array),
+    "row_rel_err_signed": ("row_rel_err", _row_rel_err_signed),
+    "row_rel_err_elementwise": ("row_rel_err", _row_rel_err_elementwise),
+    "row_rel_err_broadcasts": ("row_rel_err", _row_rel_err_broadcasts),
 }
 
 
