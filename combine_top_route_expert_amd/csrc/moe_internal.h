@@ -338,9 +338,11 @@ struct MTileMap {
 // those past their XCD's share exit.
 // xcd_tile_at: the same for position q of XCD x's sequence (a workgroup that
 // takes several tiles walks q, q + G, q + 2G, ... with G its XCD's workgroup
-// count); false once q is past the XCD's tiles.
-__device__ __forceinline__ bool xcd_tile_at(const MTileMap& tm, int n_tiles, int x, int q,
-                                            int reserve, int* mt, int* nt) {
+// count); false once q is past the XCD's tiles.  Pure integer arithmetic on
+// tm.total and tm.large, also compiled for the host so that its coverage
+// properties can be checked there.
+__host__ __device__ __forceinline__ bool xcd_tile_at(const MTileMap& tm, int n_tiles, int x, int q,
+                                                     int reserve, int* mt, int* nt) {
   const int ml = q / n_tiles;
   *nt = q - ml * n_tiles;
   const int per = (tm.large + 7) >> 3;
