@@ -5,14 +5,22 @@ A step is one moe_chunked_forward call: routing metadata for every chunk,
 then per chunk pair, on one HIP stream: one gate/up GEMM + SwiGLU launch over
 both chunks' rows that gathers its rows straight from hidden_states (the
 permute fused into its row addressing), one down GEMM launch, and the two
-chunks' weighted combines.  The per-chunk schedule (every chunk runs permute,
-FFN and combine on its own stream, two streams alternating) is timed beside it.  Inputs are seeded
-synthetic data already resident in HBM when the timed region starts.
+chunks' weighted combines.  Inputs are seeded synthetic data already resident
+in HBM when the timed region starts.
 
-Prints ONE JSON line: MoE-layer tokens/s (T / seconds per step), the roofline
-of the dominant kernel (the gate/up grouped GEMM) measured live with HIP
-events on the stream it runs on, and the CPU oracle timed on the host cores on
-a bounded sample of the same workload.
+Headline (default): the DeepSeek-V3-shaped layer (T=4096, H=7168, E=256
+routed experts, top-8, I=2048, bf16, all experts on this GPU), num_chunks=1.
+`value` is T / (mean time of K single steps, each started with L2 and MALL
+flushed by writing a 1 GiB scratch buffer outside its HIP-event window).
+Back-to-back (pipelined) steps, a replayed HIP graph, the per-chunk two-stream
+schedule, the backward and a num_chunks sweep of the packed 16k-token layer
+(time and requested workspace against the W_pair model) are reported beside
+it.
+
+Prints ONE JSON line: MoE-layer tokens/s, the roofline of the dominant kernel
+(the gate/up grouped GEMM) measured live with HIP events on the stream it runs
+on, and the CPU oracle timed on the host cores on a bounded sample of the same
+workload.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--num-chunks N]
 """
@@ -152,32 +160,40 @@ def time_graph(moe, torch, shape, inp, steps):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def per_step_times(moe, torch, shape, inp, reps, flush_bytes=0):
-    """Median and minimum of single-step times (HIP events around each step).  With
-    flush_bytes > 0 a scratch buffer of that size is written before every step,
-    outside the timed window, so L2 and MALL start cold."""
+def per_step_times(moe, torch, shape, inp, reps, flush_bytes=0, warmup=2):
+    """Single-step times: HIP events on s0 around each of `reps` steps, with a
+    device synchronisation on both sides of every step.  With flush_bytes > 0 a
+    scratch buffer of that size is written before every step, outside its
+    event window, so L2 and MALL start cold.  Returns the mean (the headline
+    rate uses it), median and minimum."""
     out = torch.empty((shape.T, shape.H), dtype=shape.torch_dtype, device="cuda")
     ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
     scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
     times = []
-    for i in range(reps + 2):
+    t_wall = 0.0
+    for i in range(reps + warmup):
         if scratch is not None:
             scratch.fill_(i & 0xff)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
         e0.record(s0)
         moe.moe_chunked_forward(shape, inp["hidden"], inp["idx"], inp["w"], inp["wgu"], inp["wd"],
-                                out, ws, None, s0=s0, s1=s1)
+                                out, ws, err, s0=s0, s1=s1)
         e1.record(s0)
         torch.cuda.synchronize()
-        if i >= 2:
+        if i >= warmup:
+            t_wall += time.perf_counter() - t0
             times.append(e0.elapsed_time(e1))
-    times.sort()
-    return {"median_ms": times[len(times) // 2], "min_ms": times[0], "reps": reps,
-            "flush_bytes": flush_bytes}
+    srt = sorted(times)
+    return {"mean_ms": sum(times) / len(times), "median_ms": srt[len(srt) // 2],
+            "min_ms": srt[0], "max_ms": srt[-1], "reps": reps, "flush_bytes": flush_bytes,
+            "wall_ms_mean": t_wall * 1e3 / reps, "dev_error": int(err.item()),
+            "workspace_bytes": ws.numel()}
 
 
 def kernel_times(moe, torch, shape, inp, reps):
@@ -260,56 +276,130 @@ def load_traffic(config_name, N):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, synth, target_s=15.0):
-    """The oracle, as it stands, on a bounded prefix of the same workload."""
-    import numpy as np
+def cpu_info():
+    """Host cores the process may use, and the CPU model."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"nproc": usable, "cpu_count": os.cpu_count(), "cpu_model": model}
+
+
+def cpu_baseline(cfg, inp, synth, torch, target_s=12.0, max_runs=4):
+    """The oracle, as it stands, on a bounded prefix of the same workload (N=1).
+
+    Expert weights are handed to the oracle one expert at a time as exact
+    float64 copies (converted on the device, then copied to the host), and
+    nothing is cached, so host memory stays bounded for every workload; the
+    time spent in those conversions is measured and left out of the oracle's
+    time.  The prefix grows until the oracle works about target_s / 3 seconds
+    (at most max_runs runs)."""
     import oracle
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] or [os.cpu_count() or 1])
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        threads = os.cpu_count() or 1
     hid = synth.to_f64(inp["hidden"])
-    cache = {}
+    conv = [0.0, 0]
 
     def get(e):
-        if e not in cache:
-            cache[e] = (synth.to_f64(inp["wgu"][e]), synth.to_f64(inp["wd"][e]))
-        return cache[e]
+        t = time.perf_counter()
+        pair = (inp["wgu"][e].to(torch.float64).cpu().numpy(),
+                inp["wd"][e].to(torch.float64).cpu().numpy())
+        conv[0] += time.perf_counter() - t
+        conv[1] += 1
+        return pair
 
     def run(ts):
-        for e in np.unique(inp["idx_np"][:ts]):
-            get(int(e))  # input conversion happens outside the timed region
+        log(f"  oracle on the first {ts} tokens")
+        conv[0], conv[1] = 0.0, 0
         t = time.perf_counter()
         oracle.moe_forward(hid[:ts], inp["idx_np"][:ts], inp["w_np"][:ts], get, cfg.E, cfg.I,
                            cfg.groups, 1)
-        return time.perf_counter() - t
+        return time.perf_counter() - t - conv[0], conv[1]
 
-    ts = min(cfg.T, 128)
-    el = run(ts)
-    while el < target_s / 3 and ts < cfg.T:
+    ts = min(cfg.T, 16)
+    el, n_exp = run(ts)
+    runs = 1
+    while el < target_s / 3 and ts < cfg.T and runs < max_runs:
         ts = min(cfg.T, max(ts * 2, int(ts * target_s / max(el, 1e-3))))
-        el = run(ts)
-    # a sample that finishes quickly is repeated until about target_s/1.5 of CPU work
+        el, n_exp = run(ts)
+        runs += 1
     reps, total = 1, el
-    while total < target_s / 1.5:
-        total += run(ts)
+    while total < target_s / 1.5 and runs < max_runs:
+        more, _ = run(ts)
+        total += more
         reps += 1
-    return {"value": ts * reps / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {ts} of {cfg.T} tokens of {cfg.name} (N=1), float64 numpy oracle, "
-                      f"{reps} run(s), {total:.1f} s; expert weights converted to float64 outside "
-                      f"the timing"}
+        runs += 1
+    d = {"value": ts * reps / total, "unit": "tokens/s", "cores": int(threads),
+         "kind": "oracle",
+         "sample": f"first {ts} of {cfg.T} tokens of {cfg.name} (N=1; {n_exp} experts touched), "
+                   f"float64 numpy oracle (oracle.moe_forward), {reps} timed run(s), "
+                   f"{total:.1f} s of oracle time; each expert's weights converted to float64 "
+                   f"one expert at a time, outside the timing"}
+    d.update(cpu_info())
+    d["blas_threads"] = int(threads)
+    return d
+
+
+def chunk_sweep(moe, torch, synth, name, Ns, steps):
+    """num_chunks sweep of one workload: time per step of both schedules and the
+    workspace the library requests, against the W_pair model
+    min(N, 2) * ceil(T/N) * k * (H + I) * element bytes (the pair residency of
+    the Chunk MoE key formulas; H + I because y overwrites the dead x_perm)."""
+    cfg = synth.CONFIGS[name]
+    log(f"chunk sweep inputs {name}")
+    inp = make_inputs(cfg, torch, synth)
+    s = cfg.elem_bytes
+    res = {"workload": name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.k, "I": cfg.I,
+           "points": []}
+    for N in Ns:
+        shape = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, N, cfg.dtype)
+        log(f"chunk sweep {name} N={N}")
+        time_layer(moe, torch, shape, inp, 1, 5)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        fused = time_layer(moe, torch, shape, inp, steps, 3)
+        peak = torch.cuda.max_memory_allocated() - base
+        per_chunk = time_layer(moe, torch, shape, inp, steps, 3,
+                               schedule=moe.MOE_SCHEDULE_PER_CHUNK)
+        model = min(N, 2) * -(-cfg.T // N) * cfg.k * (cfg.H + cfg.I) * s
+        res["points"].append({
+            "N": N, "ms_pair_fused": fused["wall_ms"], "ms_per_chunk_two_streams": per_chunk["wall_ms"],
+            "tokens_per_s_pair_fused": cfg.T / (fused["wall_ms"] * 1e-3),
+            "workspace_requested_bytes": fused["workspace_bytes"],
+            "w_pair_model_bytes": model,
+            "workspace_over_model": fused["workspace_bytes"] / model,
+            "peak_alloc_workspace_and_out_bytes": peak})
+    del inp
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="bf16_e64_zipf")
-    ap.add_argument("--num-chunks", type=int, default=2)
+    ap.add_argument("--config", default="dsv3_e256")
+    ap.add_argument("--num-chunks", type=int, default=1)
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--sweep-config", default="packed16k_e128",
+                    help="workload of the num_chunks sweep ('' to skip it)")
+    ap.add_argument("--sweep-chunks", default="1,2,4,8")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -317,7 +407,6 @@ def main():
               "GPU only (no multi-GPU path); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import combine_top_route_expert_amd as moe
@@ -331,37 +420,46 @@ def main():
     inp = make_inputs(cfg, torch, synth)
     shape = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, N, cfg.dtype)
 
-    # one common warm-up (clocks, caches, allocator) before any timed run: at
-    # least 20 steps and one second, since the GPU reaches its steady clock only
-    # after some 100 ms of load (a first timed run right after 20 steps measured
-    # 8% slower than the next ones)
+    # one common warm-up (clocks, caches, allocator) before any timed run: the
+    # W warm-up steps, then more until one second has passed, since the GPU
+    # reaches its steady clock only after some 100 ms of load (a first timed run
+    # right after 20 short steps measured 8% slower than the next ones)
     log("warm-up")
     t_warm = time.perf_counter()
-    time_layer(moe, torch, shape, inp, 1, max(args.warmup, 20))
+    time_layer(moe, torch, shape, inp, 1, max(args.warmup, 1))
     while time.perf_counter() - t_warm < 1.0:
-        time_layer(moe, torch, shape, inp, 1, 50)
-    log(f"layer N={N}")
-    main_run = time_layer(moe, torch, shape, inp, args.steps, args.warmup)
-    log(f"layer N=1 (reference)")
-    shape1 = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, 1, cfg.dtype)
-    run1 = time_layer(moe, torch, shape1, inp, args.steps, args.warmup, two_streams=False)
-    log(f"layer N={N}, per-chunk schedule")
+        time_layer(moe, torch, shape, inp, 1, 10)
+    log(f"headline: {args.steps} single steps, L2/MALL flushed before each, N={N}")
+    cold = per_step_times(moe, torch, shape, inp, args.steps, flush_bytes=1 << 30)
+    log("single steps, warm")
+    warm = per_step_times(moe, torch, shape, inp, args.steps)
+    log("back-to-back steps")
+    piped = time_layer(moe, torch, shape, inp, args.steps, args.warmup)
+    log(f"per-chunk schedule, N={N}")
     run_pc = time_layer(moe, torch, shape, inp, args.steps, args.warmup,
                         schedule=moe.MOE_SCHEDULE_PER_CHUNK)
     log("layer replayed from a HIP graph")
     graph_ms = time_graph(moe, torch, shape, inp, args.steps)
-    log("single steps, warm and with L2/MALL flushed")
-    warm = per_step_times(moe, torch, shape, inp, 20)
-    cold = per_step_times(moe, torch, shape, inp, 20, flush_bytes=1 << 30)
-    log(f"backward N={N}")
-    bwd_ms, bwd_ws = time_backward(moe, torch, shape, inp, max(5, args.steps // 5), 2)
+    bwd = None
+    if not args.no_backward:
+        log(f"backward N={N}")
+        bwd_steps = max(3, args.steps // 10)
+        bwd_ms, bwd_ws = time_backward(moe, torch, shape, inp, bwd_steps, 1)
+        A_valid = int(inp["counts"].sum())
+        bwd = {"ms_per_step": bwd_ms, "value": cfg.T / (bwd_ms * 1e-3), "steps": bwd_steps,
+               "flop_per_step": 18.0 * A_valid * cfg.H * cfg.I,
+               "tflops": 18.0 * A_valid * cfg.H * cfg.I / (bwd_ms * 1e-3) / 1e12,
+               "workspace_bytes": bwd_ws,
+               "note": "moe_chunked_backward: forward recomputed per chunk pair, grads of "
+                       "hidden_states, top_k_weights (fp32) and both expert weight tensors "
+                       "(fp32); flop = 18*A*H*I"}
+        torch.cuda.empty_cache()
     log("per-kernel timing")
     kt, rows0, e_act0, chunk_rows = kernel_times(moe, torch, shape, inp, args.kernel_reps)
     copy_bw = copy_bandwidth(torch)
 
     s = cfg.elem_bytes
     H, I = cfg.H, cfg.I
-    A_valid = int(inp["counts"].sum())
     # the gate/up launch reads each of the pair's tokens' rows (gathered from
     # hidden_states), every active expert's weights once, and writes act
     pair_tokens = min(cfg.T, 2 * -(-cfg.T // N)) if N >= 2 else cfg.T
@@ -376,12 +474,12 @@ def main():
         roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_f / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    traffic = load_traffic(cfg.name, N)
-    roof["traffic"] = traffic
+    roof["traffic"] = load_traffic(cfg.name, N)
     roof["kernel"] = ("grouped_gemm_bf16<gate_up> (moe_expert_gate_up_gather_pair), chunks 0-1"
                       if N >= 2 else
                       "grouped_gemm_bf16<gate_up> (moe_expert_gate_up_gather_pair), chunk 0")
     roof["rows_per_launch"] = rows0
+    roof["active_experts"] = e_act0
     roof["algorithmic_bytes_per_launch"] = gu_bytes
     roof["algorithmic_flop_per_launch"] = gu_flops
     roof["avg_launch_us"] = kt["gate_up"]
@@ -408,40 +506,42 @@ def main():
             r.update({"flop": flop, "TFLOPs": flop / sec / 1e12, "mfma_frac": flop / sec / peak_f})
         kernels_roofline[name] = r
 
-    ms = main_run["wall_ms"]
+    ms = cold["mean_ms"]
     line = {
         "metric": METRIC, "value": cfg.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": H, "E": cfg.E, "top_k": cfg.k,
                    "I": I, "num_chunks": N, "streams": 1, "schedule": "pair_fused",
-                   "groups": cfg.groups},
+                   "groups": cfg.groups,
+                   "timing": "mean of K single steps, each after a 1 GiB L2/MALL flush, "
+                             "HIP events on s0 with a device sync on both sides"},
         "roofline": roof,
         "kernels_us": kt,
         "kernels_roofline": kernels_roofline,
-        "event_ms_per_step": main_run["event_ms"],
-        "unchunked": {"ms_per_step": run1["wall_ms"], "value": cfg.T / (run1["wall_ms"] * 1e-3)},
+        "single_step": {"cold": cold, "warm": warm},
+        "pipelined": {"ms_per_step": piped["wall_ms"], "value": cfg.T / (piped["wall_ms"] * 1e-3),
+                      "event_ms_per_step": piped["event_ms"],
+                      "note": "K steps back to back between two device synchronisations"},
         "per_chunk_schedule": {"ms_per_step": run_pc["wall_ms"],
-                               "value": cfg.T / (run_pc["wall_ms"] * 1e-3)},
+                               "value": cfg.T / (run_pc["wall_ms"] * 1e-3),
+                               "note": "permute, gate_up, down, combine per chunk on stream c%2"},
         "hip_graph": {"ms_per_step": graph_ms, "value": cfg.T / (graph_ms * 1e-3),
                       "note": "the same step captured once and replayed"},
-        "single_step": {"warm": warm, "cold": cold},
-        "backward": {"ms_per_step": bwd_ms, "value": cfg.T / (bwd_ms * 1e-3),
-                     "flop_per_step": 18.0 * A_valid * H * I,
-                     "tflops": 18.0 * A_valid * H * I / (bwd_ms * 1e-3) / 1e12,
-                     "workspace_bytes": bwd_ws,
-                     "note": "moe_chunked_backward: forward recomputed per chunk pair, "
-                             "grads of hidden_states, top_k_weights (fp32) and both expert "
-                             "weight tensors (fp32); flop = 18*A*H*I"},
-        "workspace_bytes": {"N": main_run["workspace_bytes"], "N1": run1["workspace_bytes"],
-                            "slots_model_N": min(N, 2) * -(-cfg.T // N) * cfg.k * (H + I) * s},
+        "backward": bwd,
+        "workspace_bytes": {"requested": cold["workspace_bytes"],
+                            "slots_model": min(N, 2) * -(-cfg.T // N) * cfg.k * (H + I) * s},
         "copy_bandwidth_GBps": copy_bw / 1e9,
         "expert_load": {"max_over_mean": float(inp["counts"].max() / inp["counts"].mean()),
                         "empty_experts": int((inp["counts"] == 0).sum())},
     }
+    if args.sweep_config:
+        Ns = [int(x) for x in args.sweep_chunks.split(",") if x]
+        line["chunk_sweep"] = chunk_sweep(moe, torch, synth, args.sweep_config, Ns,
+                                          max(5, args.steps // 2))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, synth)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, synth, torch)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

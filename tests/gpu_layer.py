@@ -31,6 +31,7 @@ class Layer:
     idx_np: np.ndarray
     w_np: np.ndarray
     _f64: Dict[int, tuple] = dataclasses.field(default_factory=dict)
+    _n64: int = 0
 
     def shape(self, N: int = 1, G: Optional[int] = None) -> moe.moe_shape:
         c = self.cfg
@@ -40,12 +41,19 @@ class Layer:
         return synth.to_f64(self.hidden)
 
     def expert64(self, e: int):
-        """float64 host copy of expert e's weights (an exact copy of the input)."""
+        """float64 host copy of expert e's weights (an exact copy of the input:
+        widened to float64 on the device, then copied).  At most about 6 GiB of
+        experts are kept, so a pass over all 256 DeepSeek-V3-shaped experts
+        streams them."""
         if e not in self._f64:
             per = 8 * (self.wgu[e].numel() + self.wd[e].numel())
             if per * (len(self._f64) + 1) > (6 << 30):
                 self._f64.clear()
-            self._f64[e] = (synth.to_f64(self.wgu[e]), synth.to_f64(self.wd[e]))
+            self._f64[e] = (self.wgu[e].to(torch.float64).cpu().numpy(),
+                            self.wd[e].to(torch.float64).cpu().numpy())
+            self._n64 += 1
+            if self._n64 % 64 == 0:
+                say(f"  {self._n64} expert weight sets widened to float64 for the oracle")
         return self._f64[e]
 
 

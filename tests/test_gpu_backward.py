@@ -122,10 +122,13 @@ def test_backward_every_output_vs_oracle(name, N, T):
     check_weight_grads(L, ref, gwgu, gwd, tol)
 
 
-SAMPLED = [("bf16_e64_zipf", 2, 8, 4), ("dsv3_e256", 1, 4, 2), ("skew_two_experts", 1, 6, 2),
-           ("packed16k_e128", 4, 8, 3), ("decode_t64", 1, 6, 3)]
+# the E = 256 workloads: 32 tokens (every slot's expert fetched once per token
+# and slot by the plain-definition oracle) and 8 experts' weight gradients
+SAMPLED = [("bf16_e64_zipf", 2, 8, 4), ("dsv3_e256", 1, 32, 8), ("skew_two_experts", 1, 6, 2),
+           ("packed16k_e128", 4, 8, 3), ("decode_t64", 1, 32, 8)]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,N,n_tok,n_exp", SAMPLED)
 def test_backward_sampled_vs_oracle(name, N, n_tok, n_exp):
     L = layer_for(name)
@@ -134,7 +137,9 @@ def test_backward_sampled_vs_oracle(name, N, n_tok, n_exp):
     gh, gw, gwgu, gwd, err = run_backward(L, N, go)
     assert err == 0
     rng = np.random.default_rng(3)
-    toks = sorted({0, cfg.T - 1, *[int(t) for t in rng.integers(0, cfg.T, n_tok)]})
+    # n_tok distinct tokens (plus the first and last)
+    toks = sorted({0, cfg.T - 1, *[int(t) for t in rng.choice(cfg.T, min(n_tok, cfg.T),
+                                                              replace=False)]})
     ref_h, ref_w = oracle.moe_tokens_backward(toks, L.hidden64(), L.idx_np, L.w_np, L.expert64,
                                               cfg.E, cfg.I, f64(go))
     tol = TOL[cfg.dtype]

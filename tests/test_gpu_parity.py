@@ -244,13 +244,20 @@ def test_expert_ffn_vs_oracle(name, N, n_experts):
 # --------------------------------------------------------------------- whole layer
 FULL_CASES = [("tiny_f32", 1, None), ("t3_n4", 4, None), ("t3_n4", 1, None),
               ("bf16_e64_zipf", 1, 1024), ("bf16_e64_zipf", 2, 1000),
-              ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None), ("odd_dims_f32", 4, None)]
+              ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None), ("odd_dims_f32", 4, None),
+              # full sizes, every row: the DeepSeek-V3-shaped layer as the bench runs it (one
+              # chunk, 4096 tokens, 256 experts of 95-160 rows), the decode batch, the skew
+              ("decode_t64", 1, None), ("skew_two_experts", 1, None), ("dsv3_e256", 1, None)]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,N,T", FULL_CASES)
 def test_forward_every_row_vs_oracle(name, N, T):
+    """Every output row against the chunked float64 oracle (its experts streamed
+    one at a time for the E = 256 workloads)."""
     L = layer_for(name, T)
     cfg = L.cfg
+    say(f"forward every row {name} T={cfg.T} N={N}")
     out, err = run_forward(L, L.shape(N))
     ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
                                    cfg.groups, N)
@@ -301,8 +308,8 @@ def test_forward_largest_expert_count():
     assert torch.equal(out4, out)
 
 
-SAMPLED_CASES = [("bf16_e64_zipf", 2, 24), ("dsv3_e256", 1, 4), ("packed16k_e128", 4, 48),
-                 ("packed16k_e128", 8, 16), ("decode_t64", 1, 6), ("skew_two_experts", 1, 64)]
+SAMPLED_CASES = [("bf16_e64_zipf", 2, 24), ("dsv3_e256", 3, 24), ("packed16k_e128", 4, 48),
+                 ("packed16k_e128", 8, 16), ("skew_two_experts", 1, 64)]
 
 
 @pytest.mark.parametrize("name,N,n_tok", SAMPLED_CASES)
