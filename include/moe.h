@@ -112,7 +112,9 @@ int32_t moe_resolve_num_chunks(int32_t num_tokens, int32_t num_chunks, int32_t c
  */
 moe_status moe_chunk_range(const moe_shape* shape, int32_t chunk, int32_t* t0, int32_t* t1);
 
-/* Bytes of scratch moe_route_meta needs.  Host-only. */
+/* Bytes of scratch moe_route_meta needs: per-segment expert counts of the
+ * batched metadata pass (MindSpeed Chunk MoE article, timing-diagram section:
+ * one metadata pass for all chunks).  Host-only. */
 moe_status moe_route_meta_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /*
@@ -152,12 +154,21 @@ moe_status moe_route_meta(const moe_shape* shape, const int32_t* top_k_index, in
  * with dst_row[f] >= 0.  hidden_states and dst_row are the full [T][H] and
  * [T*k] arrays; x_perm is the chunk's buffer of at least (t1-t0)*k rows of H.
  * Rows past offsets[chunk][E] are not written.  Pure data movement (bit-exact).
+ *
+ * Implementation choice: the call takes dst_row (token-major: each token row is
+ * read once and written to its k expert rows) rather than the inverse src_row
+ * (row-major gather, x_perm[r] = hidden_states[src_row[t0*k + r] / k]); both
+ * give the same buffer.  The gather form is what moe_expert_gate_up_gather_pair
+ * fuses into its row addressing.
  */
 moe_status moe_permute(const moe_shape* shape, int32_t chunk, const void* hidden_states,
                        const int32_t* dst_row, void* x_perm, hipStream_t stream);
 
 /*
- * First expert GEMM with the SwiGLU epilogue, grouped by expert:
+ * First expert GEMM with the SwiGLU epilogue, grouped by expert (the expert
+ * computation on the permuted, expert-contiguous rows of the MindSpeed Chunk
+ * MoE article's core principle and timing diagram; the SwiGLU form is this
+ * library's reading, the pages do not give the FFN):
  * act[r][i] = silu(g) * u with g = x_perm[r] . w_gate_up[e][i],
  * u = x_perm[r] . w_gate_up[e][I+i], for the rows r in
  * [offsets[chunk][e], offsets[chunk][e+1]).  offsets is the full [N][E+1]
@@ -169,22 +180,28 @@ moe_status moe_expert_gate_up(const moe_shape* shape, int32_t chunk, const void*
                               hipStream_t stream);
 
 /*
- * Second expert GEMM, grouped by expert: y[r] = act[r] . w_down[e]^T for the
- * rows of expert e.  y is the chunk's [rows][H] buffer and may alias x_perm.
+ * Second expert GEMM, grouped by expert (same passage as moe_expert_gate_up):
+ * y[r] = act[r] . w_down[e]^T for the rows [offsets[chunk][e],
+ * offsets[chunk][e+1]) of expert e.  act is the chunk's [rows][I] buffer; y is
+ * its [rows][H] buffer and may alias x_perm.  Rows past offsets[chunk][E] are
+ * not written.
  */
 moe_status moe_expert_down(const moe_shape* shape, int32_t chunk, const void* act,
                            const int32_t* offsets, const void* w_down, void* y,
                            hipStream_t stream);
 
-/* moe_expert_gate_up followed by moe_expert_down on the same stream. */
+/* moe_expert_gate_up followed by moe_expert_down on the same stream: the whole
+ * expert step of one chunk (MindSpeed Chunk MoE article, timing diagram:
+ * Expert(c)). */
 moe_status moe_expert_ffn(const moe_shape* shape, int32_t chunk, const void* x_perm,
                           const int32_t* offsets, const void* w_gate_up, const void* w_down,
                           void* act, void* y, hipStream_t stream);
 
 /*
  * Expert GEMMs of the two chunks of a pair, chunk and chunk + 1, each as ONE
- * grouped launch over both chunks' rows (the pair residency W_pair of the
- * MindSpeed Chunk MoE key formulas: both chunks' rows are resident together, so
+ * grouped launch over both chunks' rows (the adjacent-chunk pairs of the
+ * MindSpeed Chunk MoE article's timing diagram and the pair residency W_pair of
+ * its key formulas: both chunks' rows are resident together, so
  * each expert's weights are streamed once for the pair instead of once per
  * chunk).  Row for row the same arithmetic as the single-chunk calls, so the
  * same bits.
@@ -217,11 +234,19 @@ moe_status moe_expert_gate_up_gather_pair(const moe_shape* shape, int32_t chunk,
                                           const int32_t* offsets, const void* w_gate_up,
                                           void* act, hipStream_t stream);
 
+/*
+ * Down GEMM of a chunk pair as one grouped launch (same passages as
+ * moe_expert_gate_up_pair): act is the pair's joint [rows0 + rows1][I] buffer
+ * from moe_expert_gate_up_pair; y0 / y1 receive chunk `chunk`'s and chunk
+ * `chunk+1`'s rows at their chunk-local positions (y1 ignored, may be null, when
+ * chunk + 1 == N or that chunk is empty).
+ */
 moe_status moe_expert_down_pair(const moe_shape* shape, int32_t chunk, const void* act,
                                 const int32_t* offsets, const void* w_down, void* y0, void* y1,
                                 hipStream_t stream);
 
-/* moe_expert_gate_up_pair followed by moe_expert_down_pair on the same stream. */
+/* moe_expert_gate_up_pair followed by moe_expert_down_pair on the same stream
+ * (same passages). */
 moe_status moe_expert_ffn_pair(const moe_shape* shape, int32_t chunk, const void* x_perm0,
                                const void* x_perm1, const int32_t* offsets,
                                const void* w_gate_up, const void* w_down, void* act, void* y0,
@@ -267,7 +292,8 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
                                         int32_t* dev_error, void* ws, size_t ws_bytes,
                                         hipStream_t s0, hipStream_t s1, int32_t schedule);
 
-/* moe_chunked_forward_schedule with MOE_SCHEDULE_PAIR_FUSED. */
+/* moe_chunked_forward_schedule with MOE_SCHEDULE_PAIR_FUSED.  That schedule runs
+ * every step on s0; s1 is accepted (and may be null) but not used. */
 moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states,
                                const int32_t* top_k_index, const float* top_k_weights,
                                const void* w_gate_up, const void* w_down, void* out,
