@@ -25,6 +25,7 @@ __all__ = [
     "moe_chunked_forward_schedule", "moe_backward_workspace_size", "moe_chunked_backward",
     "moe_unpermute_combine_backward", "moe_permute_backward", "MOE_F32", "MOE_BF16",
     "MOE_SCHEDULE_PAIR_FUSED", "MOE_SCHEDULE_PER_CHUNK", "EXPORTED_SYMBOLS",
+    "moe_chunked_forward_noalloc",
 ]
 
 MOE_F32, MOE_BF16 = 0, 1
@@ -37,7 +38,8 @@ EXPORTED_SYMBOLS = (
     "moe_route_meta_workspace_size", "moe_workspace_size", "moe_route_meta", "moe_permute",
     "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn", "moe_expert_gate_up_pair",
     "moe_expert_gate_up_gather_pair", "moe_expert_down_pair", "moe_expert_ffn_pair", "moe_unpermute_combine",
-    "moe_chunked_forward", "moe_chunked_forward_schedule", "moe_backward_workspace_size",
+    "moe_chunked_forward", "moe_chunked_forward_schedule", "moe_chunked_forward_noalloc",
+    "moe_backward_workspace_size",
     "moe_chunked_backward", "moe_unpermute_combine_backward", "moe_permute_backward",
 )
 
@@ -132,6 +134,7 @@ def load_library() -> ctypes.CDLL:
         "moe_chunked_forward_schedule": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P,
                                                         ctypes.c_size_t, _P, _P,
                                                         ctypes.c_int32]),
+        "moe_chunked_forward_noalloc": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P]),
         "moe_backward_workspace_size": (ctypes.c_int, [_SP, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_chunked_backward": (ctypes.c_int, [_SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                 _P, _P, ctypes.c_size_t, _P, _P]),
@@ -377,6 +380,22 @@ def moe_chunked_forward(shape: moe_shape, hidden_states, top_k_index, top_k_weig
                         w_down, out, ws, dev_error=None, s0=None, s1=None) -> None:
     moe_chunked_forward_schedule(shape, hidden_states, top_k_index, top_k_weights, w_gate_up,
                                  w_down, out, ws, dev_error, s0, s1, _fn="moe_chunked_forward")
+
+
+def moe_chunked_forward_noalloc(shape: moe_shape, hidden_states, top_k_index, top_k_weights,
+                                w_gate_up, w_down, out, dev_error=None, stream=None) -> None:
+    """The forward layer with the library's own static 64 MiB device scratch as
+    its workspace (no allocation in the call); calls on one GPU must not
+    overlap."""
+    dt = shape.torch_dtype
+    T, H, E, k, I = shape.T, shape.H, shape.E, shape.k, shape.I  # noqa: E741
+    _check("moe_chunked_forward_noalloc", load_library().moe_chunked_forward_noalloc(
+        ctypes.byref(shape), _ptr(hidden_states, dt, T * H, "hidden_states"),
+        _ptr(top_k_index, torch.int32, T * k, "top_k_index"),
+        _ptr(top_k_weights, torch.float32, T * k, "top_k_weights"),
+        _ptr(w_gate_up, dt, E * 2 * I * H, "w_gate_up"), _ptr(w_down, dt, E * H * I, "w_down"),
+        _ptr(out, dt, T * H, "out"), _ptr(dev_error, torch.int32, 0, "dev_error"),
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------- backward

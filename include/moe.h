@@ -300,6 +300,25 @@ moe_status moe_chunked_forward(const moe_shape* shape, const void* hidden_states
                                int32_t* dev_error, void* ws, size_t ws_bytes, hipStream_t s0,
                                hipStream_t s1);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * layer of moe_chunked_forward (pair-fused schedule, every step on `stream`,
+ * same bits) with no workspace argument.  Its workspace is a file-scope device
+ * array of 64 MiB (67108864 bytes) inside the library, one per GPU, held from
+ * the first call on that GPU until the process ends; the call itself
+ * allocates nothing.  Shapes whose moe_workspace_size exceeds 64 MiB return
+ * MOE_ERR_WORKSPACE_TOO_SMALL before any work is enqueued (decode-sized
+ * batches fit: T = 64, H = 7168, I = 2048, top-8 needs about 10 MB).  All calls
+ * on one GPU share that array, which keeps the last call's contents: calls that
+ * may overlap in time on one GPU race and must be ordered by the caller.
+ * Other arguments and errors as for moe_chunked_forward.
+ */
+moe_status moe_chunked_forward_noalloc(const moe_shape* shape, const void* hidden_states,
+                                       const int32_t* top_k_index, const float* top_k_weights,
+                                       const void* w_gate_up, const void* w_down, void* out,
+                                       int32_t* dev_error, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Backward of the same layer (gradient of L = sum(grad_out * out)), chunk pair
  * by chunk pair with each chunk's forward recomputed instead of stored (the
