@@ -51,11 +51,13 @@
 // Epilogue: the accumulators go through the freed stage buffers as a
 // row-major bf16 tile and leave as 16-byte row segments (store_tile_lds).
 //
-// Small tiles: an m-tile of at most 32, 64 or 128 rows (a small expert's only
-// tile) has little MFMA work and is bound by streaming its weight panel, so it
-// runs a K loop with a compact stage layout (its rows of A, then B) and three
-// stages, two in flight (k_loop_small): 41 -> 33 us per gate/up tile of at
-// most 32 rows on the Zipf workload.
+// Small tiles: an m-tile of at most 32, 64, 128 or 160 rows (a small expert's
+// only tile) has little MFMA work and is bound by streaming its weight panel, so
+// it runs a K loop with a compact stage layout (its rows of A, then B) and three
+// stages, two in flight (k_loop_small): 41 -> 33 us per gate/up tile of at most
+// 32 rows on the Zipf workload; the 160-row case (three 52 KB stages, 156 KB of
+// LDS) took the DeepSeek-V3-shaped layer, whose experts hold 95-160 rows, from
+// 4.89 to 4.79 ms (down 1724 -> 1683 us).
 //
 // What bounds it (measured with per-workgroup timestamps): the MFMA loop alone
 // (no global loads) runs at ~94% of the matrix peak at the clock it gets, and
@@ -410,17 +412,17 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
   }
 }
 
-// The K loop of a tile with at most SROWS (32 or 64) rows: such a tile (a
-// small expert's only m-tile) is bound by streaming its B panel rather than by
-// MFMAs, so it uses the compact stage layout and SSTAGES stages (SSTAGES - 1 in
-// flight) to keep more weight bytes in flight.  kMfma: the wave holds the
-// tile's rows (wave row 0, F = SROWS / 32 blocks); the other waves only load
-// and join the barriers.
-template <bool kMfma, int SROWS, int SSTAGES, int FM, int FN, int WN, int BK, class Loader>
+// The K loop of a tile with at most SROWS (32, 64, 128 or 160) rows: such a
+// tile (a small expert's only m-tile) is bound by streaming its B panel rather
+// than by MFMAs, so it uses the compact stage layout and SSTAGES stages
+// (SSTAGES - 1 in flight) to keep more weight bytes in flight.  The wave holds
+// F 32-row blocks of the tile's rows starting at row0 (its band); a wave with
+// F = 0 only loads and joins the barriers.
+template <int F, int SROWS, int SSTAGES, int FM, int FN, int WN, int BK, class Loader>
 __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
-                                             int KT, int per_stage, int lane, int wn) {
+                                             int KT, int per_stage, int lane, int wn, int row0) {
   using G = StageGeom<BK>;
-  constexpr int F = SROWS / 32;
+  constexpr bool kMfma = F > 0;
   constexpr int STAGE = Loader::template small_stage<SROWS>();
 #pragma unroll
   for (int s = 0; s < SSTAGES - 1; ++s)
@@ -437,9 +439,10 @@ __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int fo = G::frag_offset(lane, kk);
-        bf16x8 af[F], bfr[FN];
+        bf16x8 af[F > 0 ? F : 1], bfr[FN];
 #pragma unroll
-        for (int i = 0; i < F; ++i) af[i] = *(const bf16x8*)(sa + i * 32 * G::ROW_BYTES + fo);
+        for (int i = 0; i < F; ++i)
+          af[i] = *(const bf16x8*)(sa + (row0 + i * 32) * G::ROW_BYTES + fo);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
@@ -469,7 +472,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   static_assert((STAGES - 2) * (Loader::LA + Loader::LB) <= 24, "wait_loads range");
   constexpr int kSmemBytes =
       cmax(STAGES * Loader::STAGE_BYTES,
-           FM >= 4 ? cmax(3 * Loader::template small_stage<128>(),
+           FM >= 4 ? cmax(3 * Loader::template small_stage<160>(),
                           cmax(3 * Loader::template small_stage<32>(),
                                3 * Loader::template small_stage<64>()))
                    : 0);
@@ -504,27 +507,25 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
     const int KT = a.K / BK;
-    // tiles of at most 32, 64 or 128 rows: three compact stages (a fourth stage
-    // for the 32-row tiles, in 16 KB more LDS, measured no faster; the 128-row
-    // case, 144 KB, took the DeepSeek-V3-shaped layer's gate/up from 3.18 to
-    // 3.01 ms, its experts holding 95-160 rows each)
+    // tiles of at most 32, 64, 128 or 160 rows: three compact stages (a fourth
+    // stage for the 32-row tiles, in 16 KB more LDS, measured no faster; the
+    // 128-row case, 144 KB, took the DeepSeek-V3-shaped layer's gate/up from 3.18
+    // to 3.01 ms, its experts holding 95-160 rows each, and the 160-row case,
+    // 156 KB, the layer from 4.89 to 4.79 ms)
     constexpr bool kSmallPath = FM >= 4 && WAVES_M == 2;
+#define MOE_K_SMALL(F, SR) \
+  k_loop_small<F, SR, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn, wm * WM)
     if (kSmallPath && tr.rows <= 32) {
-      if (wm == 0)
-        k_loop_small<true, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-      else
-        k_loop_small<false, 32, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+      if (wm == 0) MOE_K_SMALL(1, 32); else MOE_K_SMALL(0, 32);
     } else if (kSmallPath && tr.rows <= 64) {
-      if (wm == 0)
-        k_loop_small<true, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-      else
-        k_loop_small<false, 64, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+      if (wm == 0) MOE_K_SMALL(2, 64); else MOE_K_SMALL(0, 64);
     } else if (kSmallPath && tr.rows <= 128) {
-      if (wm == 0)
-        k_loop_small<true, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
-      else
-        k_loop_small<false, 128, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn);
+      if (wm == 0) MOE_K_SMALL(4, 128); else MOE_K_SMALL(0, 128);
+    } else if (kSmallPath && tr.rows <= 160) {
+      // the second wave row holds rows 128..159: one block
+      if (wm == 0) MOE_K_SMALL(4, 160); else MOE_K_SMALL(1, 160);
     } else {
+#undef MOE_K_SMALL
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s)
         if (s < KT) ld.issue(smem, s, s);
