@@ -388,6 +388,41 @@ def chunk_sweep(moe, torch, synth, name, Ns, steps):
     return res
 
 
+def prefetch_ab(moe, torch, synth, name, base_cfg, base_inp, rounds=3, steps=20):
+    """The pair-fused schedule with and without the weight warm-up on a second
+    stream (MOE_SCHEDULE_PAIR_FUSED_PREFETCH), interleaved over `rounds`, on one
+    workload; its expert weights are reused from the headline inputs when they are
+    the same tensors."""
+    cfg = synth.CONFIGS[name]
+    same_w = (cfg.weight_seed, cfg.E, cfg.H, cfg.I, cfg.dtype) == \
+        (base_cfg.weight_seed, base_cfg.E, base_cfg.H, base_cfg.I, base_cfg.dtype)
+    if name == base_cfg.name:
+        inp = base_inp
+    else:
+        import numpy as np
+        idx, w = synth.routing(cfg)
+        inp = {"hidden": synth.hidden_states(cfg, "cuda"), "idx": torch.from_numpy(idx).cuda(),
+               "w": torch.from_numpy(w).cuda()}
+        if same_w:
+            inp["wgu"], inp["wd"] = base_inp["wgu"], base_inp["wd"]
+        else:
+            inp["wgu"], inp["wd"] = synth.all_expert_weights(cfg, "cuda")
+    shape = moe.make_shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.groups, cfg.num_chunks[0],
+                           cfg.dtype)
+    res = {"default": [], "prefetch": []}
+    for _ in range(rounds):
+        res["default"].append(time_layer(moe, torch, shape, inp, steps, 3)["wall_ms"])
+        res["prefetch"].append(time_layer(moe, torch, shape, inp, steps, 3,
+                                          schedule=moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH)["wall_ms"])
+    med = {k: sorted(v)[len(v) // 2] for k, v in res.items()}
+    return {"workload": name, "num_chunks": shape.N, "ms_default": res["default"],
+            "ms_prefetch": res["prefetch"], "median_default_ms": med["default"],
+            "median_prefetch_ms": med["prefetch"],
+            "prefetch_over_default": med["prefetch"] / med["default"],
+            "note": "back-to-back steps; the prefetch schedule warms the first 128 bytes of every "
+                    "gate/up weight row on s1 during the metadata pass"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +435,7 @@ def main():
                     help="workload of the num_chunks sweep ('' to skip it)")
     ap.add_argument("--sweep-chunks", default="1,2,4,8")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-prefetch-ab", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -535,6 +571,10 @@ def main():
         "expert_load": {"max_over_mean": float(inp["counts"].max() / inp["counts"].mean()),
                         "empty_experts": int((inp["counts"] == 0).sum())},
     }
+    if not args.no_prefetch_ab:
+        log("prefetch schedule A/B")
+        line["prefetch_schedule_ab"] = [prefetch_ab(moe, torch, synth, n, cfg, inp)
+                                        for n in ("decode_t64", cfg.name)]
     if args.sweep_config:
         Ns = [int(x) for x in args.sweep_chunks.split(",") if x]
         line["chunk_sweep"] = chunk_sweep(moe, torch, synth, args.sweep_config, Ns,

@@ -18,7 +18,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Layout of the moe_chunked_forward workspace.
 struct FwdPlan {
-  size_t counts, offsets, splits, src_row, dst_row, dev_err, meta_ws;
+  size_t counts, offsets, splits, src_row, dst_row, dev_err, sink, meta_ws;
   size_t slot[2];          // x_perm / y region of each slot
   size_t slot_act[2];      // act region of each slot
   size_t bytes;
@@ -40,6 +40,7 @@ FwdPlan fwd_plan(const Shape& s) {
   p.src_row = take((size_t)s.A * 4);
   p.dst_row = take((size_t)s.A * 4);
   p.dev_err = take(4);
+  p.sink = take(4);  // the weight warm-up's scratch word
   p.meta = meta_plan(s);
   p.meta_ws = take(p.meta.bytes);
   const size_t rows = (size_t)s.Tc * s.k;
@@ -723,7 +724,8 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
   Shape s;
   moe_status st = resolve_shape(shape, &s);
   if (st != MOE_OK) return st;
-  if (schedule != MOE_SCHEDULE_PAIR_FUSED && schedule != MOE_SCHEDULE_PER_CHUNK)
+  if (schedule != MOE_SCHEDULE_PAIR_FUSED && schedule != MOE_SCHEDULE_PER_CHUNK &&
+      schedule != MOE_SCHEDULE_PAIR_FUSED_PREFETCH)
     return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   if (!aligned(dev_error, 4)) return MOE_ERR_INVALID_ARG;
@@ -744,16 +746,32 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
   int32_t* dst_row = (int32_t*)(w + p.dst_row);
   int32_t* err = dev_error ? dev_error : (int32_t*)(w + p.dev_err);
 
+  // the prefetch schedule: s1 (ordered after the caller's work on s0) warms the
+  // head of every gate/up weight row while s0 runs the metadata pass
+  const bool warm = (schedule == MOE_SCHEDULE_PAIR_FUSED_PREFETCH && s1 != nullptr &&
+                     s1 != s0 && s.T > 0);
+  hipEvent_t ev[kEvents] = {};
+  hipError_t he = hipSuccess;
+  if (warm) {
+    he = thread_events(ev);
+    if (he == hipSuccess) he = join(s1, s0, ev[2]);
+    const int64_t row_bytes = (int64_t)s.H * s.elem;
+    if (he == hipSuccess)
+      he = launch_warm_weights(w_gate_up, (int64_t)s.E * 2 * s.I, row_bytes,
+                               (int)(row_bytes < 128 ? row_bytes : 128),
+                               (int32_t*)(w + p.sink), s1);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+  }
+
   // one metadata pass for every chunk, on s0
-  hipError_t he = launch_route_meta(s, top_k_index, counts, offsets, splits, src_row, dst_row,
-                                    err, w + p.meta_ws, s0);
+  he = launch_route_meta(s, top_k_index, counts, offsets, splits, src_row, dst_row, err,
+                         w + p.meta_ws, s0);
   if (he != hipSuccess) return MOE_ERR_HIP;
   if (s.T == 0) return MOE_OK;
 
-  // only the per-chunk schedule uses s1
+  // the per-chunk schedule runs odd chunks on s1
   const bool two = (s1 != nullptr && s1 != s0 && s.N >= 2 &&
                     schedule == MOE_SCHEDULE_PER_CHUNK);
-  hipEvent_t ev[kEvents] = {};
   if (two) {
     he = thread_events(ev);
     if (he == hipSuccess) he = join(s1, s0, ev[0]);  // s1 starts after the metadata
@@ -766,7 +784,7 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
     return (int64_t)(*t1 - *t0) * s.k;
   };
 
-  if (schedule == MOE_SCHEDULE_PAIR_FUSED) {
+  if (schedule != MOE_SCHEDULE_PER_CHUNK) {
     // Pair (c, c+1): one gate_up launch over the pair's rows (gathering them
     // from hidden_states), one down launch, one combine launch for both
     // chunks, all on s0.  Every expert's weights are streamed once per pair.
@@ -830,8 +848,8 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
       if (he != hipSuccess) return MOE_ERR_HIP;
     }
   }
-  if (two && used_s1) {
-    he = join(s0, s1, ev[1]);
+  if ((two && used_s1) || warm) {
+    he = join(s0, s1, ev[1]);  // s0 is ordered after everything on s1
     if (he != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

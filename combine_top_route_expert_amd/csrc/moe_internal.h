@@ -85,6 +85,12 @@ hipError_t launch_combine_pair(const Shape& s, int t0, int t_mid, int t1, const 
                                const void* y1, const int32_t* dst_row, const float* w,
                                void* out, hipStream_t st);
 
+// ---- weight warm-up (prefetch.hip) -------------------------------------------
+// Reads the first head_bytes (a multiple of 16) of each of `rows` rows of
+// row_bytes so they sit in the caches; writes nothing but, at most, *sink.
+hipError_t launch_warm_weights(const void* w, int64_t rows, int64_t row_bytes, int head_bytes,
+                               int32_t* sink, hipStream_t st);
+
 // ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----------------------------
 // One grouped GEMM over the rows of one chunk, or of the two chunks of a pair.
 // Expert e's rows are the chunk-0 block [off0[e], off0[e+1]) followed by the

@@ -78,7 +78,8 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Stream schedule of moe_chunked_forward_schedule (see there). */
 typedef enum moe_schedule {
   MOE_SCHEDULE_PAIR_FUSED = 0,  /* one expert-GEMM launch pair per chunk pair (default) */
-  MOE_SCHEDULE_PER_CHUNK = 1    /* every chunk runs all four steps on its own stream */
+  MOE_SCHEDULE_PER_CHUNK = 1,   /* every chunk runs all four steps on its own stream */
+  MOE_SCHEDULE_PAIR_FUSED_PREFETCH = 2  /* pair-fused, plus a weight warm-up on s1 */
 } moe_schedule;
 
 /* Problem shape.  Field names follow the pages' notation. */
@@ -281,6 +282,12 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  *  MOE_SCHEDULE_PER_CHUNK: chunk c runs permute -> gate_up -> down -> combine on
  *    stream s[c % 2] in slot c % 2, so the two chunks of a pair overlap as whole
  *    pipelines; every chunk streams the expert weights again.
+ *  MOE_SCHEDULE_PAIR_FUSED_PREFETCH: the pair-fused schedule on s0, while s1
+ *    (after the work already on s0) reads the first 128 bytes of every expert's
+ *    gate/up weight rows into the caches during the metadata pass (Ascend
+ *    dual-stream article, "02 Weight預取雙流並行": weights prefetched on a second
+ *    stream while the first is busy).  Same bits; without a distinct s1 it is the
+ *    pair-fused schedule.
  * s1 == s0 (or null) is legal and gives the same bits without overlap; the
  * result never depends on N or on the schedule.  On return s0 is ordered after
  * all work of the call.  ws must hold moe_workspace_size bytes.  dev_error is

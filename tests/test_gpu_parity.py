@@ -333,11 +333,32 @@ def test_chunked_equals_unchunked_bitwise(name, Ns):
     L = layer_for(name)
     base, _ = run_forward(L, L.shape(1), two_streams=False)
     for N in Ns:
-        for sched in (moe.MOE_SCHEDULE_PAIR_FUSED, moe.MOE_SCHEDULE_PER_CHUNK):
+        for sched in (moe.MOE_SCHEDULE_PAIR_FUSED, moe.MOE_SCHEDULE_PER_CHUNK,
+                      moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH):
             for two in (True, False):
                 say(f"chunked {name} N={N} schedule={sched} two_streams={two}")
                 out, _ = run_forward(L, L.shape(N), two_streams=two, schedule=sched)
                 assert torch.equal(out, base), (N, sched, two)
+
+
+@pytest.mark.parametrize("name,N", [("decode_t64", 1), ("bf16_e64_zipf", 2), ("tiny_f32", 3)])
+def test_prefetch_schedule_same_bits_and_oracle(name, N):
+    """The weight-prefetch schedule (gate/up weight heads warmed on s1 during the
+    metadata pass) gives the bits of the default schedule, and sampled tokens
+    match the oracle."""
+    L = layer_for(name)
+    cfg = L.cfg
+    say(f"prefetch schedule {name} N={N}: default")
+    base, _ = run_forward(L, L.shape(N), two_streams=False)
+    say(f"prefetch schedule {name} N={N}: prefetch on s1")
+    out, err = run_forward(L, L.shape(N), two_streams=True,
+                           schedule=moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH)
+    assert err == 0
+    assert torch.equal(out, base)
+    toks = sample_tokens(cfg.T, 16)
+    ref = oracle.moe_tokens(toks, L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I)
+    e = oracle.row_rel_err(f64(out[toks]), ref)
+    assert e <= TOL[cfg.dtype], e
 
 
 def test_tile_loop_several_tiles_per_workgroup():
