@@ -102,9 +102,12 @@ def check_weight_grads(L, ref, gwgu, gwd, tol, experts=None):
 
 FULL = [("tiny_f32", 1, None), ("tiny_f32", 3, None), ("t3_n4", 4, None),
         ("bf16_e64_zipf", 2, 256), ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None),
-        ("odd_dims_f32", 4, None)]
+        ("odd_dims_f32", 4, None),
+        # full size, every output: 4096 tokens over 64 Zipf-skewed experts, a chunk pair
+        ("bf16_e64_zipf", 2, None)]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,N,T", FULL)
 def test_backward_every_output_vs_oracle(name, N, T):
     L = layer_for(name, T)

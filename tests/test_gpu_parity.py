@@ -247,7 +247,10 @@ FULL_CASES = [("tiny_f32", 1, None), ("t3_n4", 4, None), ("t3_n4", 1, None),
               ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None), ("odd_dims_f32", 4, None),
               # full sizes, every row: the DeepSeek-V3-shaped layer as the bench runs it (one
               # chunk, 4096 tokens, 256 experts of 95-160 rows), the decode batch, the skew
-              ("decode_t64", 1, None), ("skew_two_experts", 1, None), ("dsv3_e256", 1, None)]
+              ("decode_t64", 1, None), ("skew_two_experts", 1, None), ("dsv3_e256", 1, None),
+              # the Zipf workloads at full size: the bench's earlier headline at N=2, and the
+              # packed 16k-token layer unchunked and at N=8 (four chunk pairs)
+              ("bf16_e64_zipf", 2, None), ("packed16k_e128", 1, None), ("packed16k_e128", 8, None)]
 
 
 @pytest.mark.timeout(900)
