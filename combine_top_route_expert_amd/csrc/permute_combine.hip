@@ -13,6 +13,10 @@
 //    row is written by exactly one wave, so no atomics are needed.
 //  * combine reads the token's k expert-output rows, accumulates
 //    w[t,j] * y[row_j] in fp32 in ascending j, and rounds once on the store.
+//    Every y row is read once and every out row written once, so the bf16
+//    combine uses non-temporal loads and stores (streaming hints): 111.6 -> 98.0
+//    us (5.4 TB/s, 67% of HBM peak) on the DeepSeek-V3-shaped layer, 119 -> 103
+//    us on the packed 16k-token layer; the permute measured 3% slower with them.
 // Both are HBM-bound: permute moves T*H*s + A*H*s bytes, combine A*H*s + T*H*s.
 // The backward reuses combine_rows with unit weights (the permute's backward is
 // a gather-sum of a token's k rows) and adds combine_backward below.
@@ -113,7 +117,7 @@ combine_rows(const u32x4* __restrict__ y0, const u32x4* __restrict__ y1, int t_m
 #pragma unroll
         for (int i = 0; i < kVecPerLane; ++i) {
           const int v = v0 + i * 64 + lane;
-          if (v < nvec) rows[g][i] = src[v];
+          if (v < nvec) rows[g][i] = __builtin_nontemporal_load(&src[v]);
         }
       }
 #pragma unroll
@@ -142,7 +146,7 @@ combine_rows(const u32x4* __restrict__ y0, const u32x4* __restrict__ y1, int t_m
       int v = v0 + i * 64 + lane;
       if (v < nvec) {
         if constexpr (kBf16) {
-          dst[v] = pack_bf16x8(acc[i]);
+          __builtin_nontemporal_store(pack_bf16x8(acc[i]), &dst[v]);
         } else {
           u32x4 q;
 #pragma unroll
