@@ -72,6 +72,7 @@
 // workloads); the size-balanced, interleaved tile order (xcd_tile); the staged
 // epilogue; the compact small-tile loop.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -232,11 +233,19 @@ struct TileLoader {
     else
       __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + koff), (lds_void*)dst, 16, 0, 0);
   }
+  // kNt: the weight panel is read by this tile only (its expert has one m-tile),
+  // so its bytes are streamed with the non-temporal cache policy.
+  template <bool kNt>
   __device__ __forceinline__ void load_b(int t, int koff, char* dst) const {
-    if constexpr (kBuf)
-      buffer_load_lds16(rb, dst, b_off[t], koff);
-    else
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + koff), (lds_void*)dst, 16, 0, 0);
+    if constexpr (kBuf) {
+      if constexpr (kNt)
+        buffer_load_lds16_nt(rb, dst, b_off[t], koff);
+      else
+        buffer_load_lds16(rb, dst, b_off[t], koff);
+    } else {
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + koff), (lds_void*)dst, 16, 0,
+                                       kNt ? 2 : 0);
+    }
   }
 
   // Compact stage of a tile with at most SROWS rows: those rows of A (the
@@ -245,7 +254,7 @@ struct TileLoader {
   static constexpr int small_a() { return SROWS * G::ROW_BYTES; }
   template <int SROWS>
   static constexpr int small_stage() { return small_a<SROWS>() + BN * G::ROW_BYTES; }
-  template <int SROWS>
+  template <int SROWS, bool kNt>
   __device__ __forceinline__ void issue_small(char* smem, int kt, int buf) const {
     char* base = smem + buf * small_stage<SROWS>();
     const int koff = kt * G::ROW_BYTES;
@@ -254,12 +263,14 @@ struct TileLoader {
       if (t < live_a)  // blocks past the tile's (at most SROWS) rows are not live
         load_a(t, koff, base + (wave * LA + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < LB; ++t) load_b(t, koff, base + small_a<SROWS>() + (wave * LB + t) * 1024);
+    for (int t = 0; t < LB; ++t)
+      load_b<kNt>(t, koff, base + small_a<SROWS>() + (wave * LB + t) * 1024);
   }
 
   // Loads one stage.  A blocks of 1 KB that lie wholly past the tile's rows are
   // not loaded (their LDS rows feed only outputs that are never stored), so a
   // wave issues live_a + LB loads per stage.
+  template <bool kNt>
   __device__ __forceinline__ void issue(char* smem, int kt, int buf) const {
     char* base = smem + buf * STAGE_BYTES;
     const int koff = kt * G::ROW_BYTES;
@@ -267,7 +278,8 @@ struct TileLoader {
     for (int t = 0; t < LA; ++t)
       if (t < live_a) load_a(t, koff, base + (wave * LA + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < LB; ++t) load_b(t, koff, base + BM * G::ROW_BYTES + (wave * LB + t) * 1024);
+    for (int t = 0; t < LB; ++t)
+      load_b<kNt>(t, koff, base + BM * G::ROW_BYTES + (wave * LB + t) * 1024);
   }
 };
 
@@ -345,13 +357,20 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
     for (int ch = threadIdx.x; ch < BM * CPR; ch += NT) {
       const int r = ch / CPR, c = (ch % CPR) * 8;
       if (r >= tr.rows || col0 + c >= a.ncols) continue;
-      const uint4 v = *(const uint4*)(smem + lds_at(r, c));
+      typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+      const u32x4v v = *(const u32x4v*)(smem + lds_at(r, c));
       uint16_t* dst;
       if (plane == 0)
         dst = (uint16_t*)row_ptr(cbase, a.c_split, tr, tr.v0 + r, a.ncols);
       else  // g (plane 1) or u (plane 2) of the joint [rows][2I] copy
         dst = a.gu + (int64_t)tr.joint_row(tr.v0 + r) * (2 * a.I) + (plane - 1) * a.I;
-      *(uint4*)(dst + col0 + c) = v;
+      // each output row is written once and read by the next launch: streamed
+      // non-temporally in the forward (act, y); the backward's recompute keeps
+      // plain stores for the g and u planes it reads back
+      if constexpr (PLANES == 1)
+        __builtin_nontemporal_store(v, (u32x4v*)(dst + col0 + c));
+      else
+        *(u32x4v*)(dst + col0 + c) = v;
     }
   }
 }
@@ -361,7 +380,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
 // stage's loads and joins every barrier.  The loop body holds no branch, so
 // the compiler schedules the fragment reads, MFMAs and the next stage's loads
 // as one block.
-template <int F, int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, class Loader>
+template <int F, int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, bool kNt, class Loader>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
                                        int KT, int per_stage, int lane, int wm, int wn) {
   using G = StageGeom<BK>;
@@ -390,7 +409,8 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
           bfr[b][j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
       };
       frag(0, 0);  // ahead of the next stage's loads, so the first MFMAs start sooner
-      if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      if (kt + STAGES - 1 < KT)
+        ld.template issue<kNt>(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         if (kk + 1 < KS) frag(kk + 1, (kk + 1) & 1);
@@ -405,7 +425,8 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      if (kt + STAGES - 1 < KT) ld.issue(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      if (kt + STAGES - 1 < KT)
+        ld.template issue<kNt>(smem, kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
     }
     // this stage's LDS reads are complete before any wave refills its buffer
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -418,7 +439,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
 // (SSTAGES - 1 in flight) to keep more weight bytes in flight.  The wave holds
 // F 32-row blocks of the tile's rows starting at row0 (its band); a wave with
 // F = 0 only loads and joins the barriers.
-template <int F, int SROWS, int SSTAGES, int FM, int FN, int WN, int BK, class Loader>
+template <int F, int SROWS, int SSTAGES, int FM, int FN, int WN, int BK, bool kNt, class Loader>
 __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
                                              int KT, int per_stage, int lane, int wn, int row0) {
   using G = StageGeom<BK>;
@@ -426,13 +447,13 @@ __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader
   constexpr int STAGE = Loader::template small_stage<SROWS>();
 #pragma unroll
   for (int s = 0; s < SSTAGES - 1; ++s)
-    if (s < KT) ld.template issue_small<SROWS>(smem, s, s);
+    if (s < KT) ld.template issue_small<SROWS, kNt>(smem, s, s);
   for (int kt = 0; kt < KT; ++kt) {
     const int newer = KT - 1 - kt < SSTAGES - 2 ? KT - 1 - kt : SSTAGES - 2;
     wait_loads(newer * per_stage);
     __builtin_amdgcn_s_barrier();
     if (kt + SSTAGES - 1 < KT)
-      ld.template issue_small<SROWS>(smem, kt + SSTAGES - 1, (kt + SSTAGES - 1) % SSTAGES);
+      ld.template issue_small<SROWS, kNt>(smem, kt + SSTAGES - 1, (kt + SSTAGES - 1) % SSTAGES);
     if constexpr (kMfma) {
       const char* sa = smem + (kt % SSTAGES) * STAGE;
       const char* sb = sa + Loader::template small_a<SROWS>();
@@ -513,8 +534,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     // to 3.01 ms, its experts holding 95-160 rows each, and the 160-row case,
     // 156 KB, the layer from 4.89 to 4.79 ms)
     constexpr bool kSmallPath = FM >= 4 && WAVES_M == 2;
+    // The weight panel of a tile that holds all of its expert's rows is read by
+    // no other tile of the launch, so it is streamed non-temporally (decode
+    // 3.28 -> 2.95 ms with the stores below); panels shared by several m-tiles
+    // of one expert stay cached (non-temporal there cost the two-expert skew 13%).
+    auto run_k = [&](auto nt_tag) __attribute__((always_inline)) {
+    constexpr bool kNt = decltype(nt_tag)::value;
 #define MOE_K_SMALL(F, SR) \
-  k_loop_small<F, SR, 3, FM, FN, WN, BK, Loader>(acc, ld, smem, KT, per_stage, lane, wn, wm * WM)
+  k_loop_small<F, SR, 3, FM, FN, WN, BK, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wn, wm * WM)
     if (kSmallPath && tr.rows <= 32) {
       if (wm == 0) MOE_K_SMALL(1, 32); else MOE_K_SMALL(0, 32);
     } else if (kSmallPath && tr.rows <= 64) {
@@ -528,7 +555,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
 #undef MOE_K_SMALL
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s)
-        if (s < KT) ld.issue(smem, s, s);
+        if (s < KT) ld.template issue<kNt>(smem, s, s);
       // 32-row blocks of this wave's band that hold rows of the tile.  Blocks past
       // them feed only outputs that are never stored, so a wide tile skips their
       // MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block loop, 3 runs
@@ -537,7 +564,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       const int band_rows = tr.rows - wm * WM;
       const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
 #define MOE_K_LOOP(F) \
-      k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
+      k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
       if constexpr (FM == 1) {
         MOE_K_LOOP(1);
       } else {
@@ -552,6 +579,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       }
 #undef MOE_K_LOOP
     }
+    };
+    if (tr.single)
+      run_k(std::true_type{});
+    else
+      run_k(std::false_type{});
     static_assert(BM * (kGateUp ? BN / 2 : BN) * 2 <= STAGES * Loader::STAGE_BYTES,
                   "C tile fits the stage buffers");
     __syncthreads();  // every wave is done with the stage buffers

@@ -40,10 +40,17 @@ __device__ __forceinline__ void buffer_load_lds16(rsrc_t r, char* dst, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
                                            off, soff, 0, 0);
 }
+// The same with the non-temporal cache policy (bytes read once: streamed past
+// the caches instead of kept).
+__device__ __forceinline__ void buffer_load_lds16_nt(rsrc_t r, char* dst, uint32_t off, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           off, soff, 0, 2);
+}
 #else
 struct rsrc_t {};
 __device__ __forceinline__ rsrc_t raw_rsrc(const void*) { return {}; }
 __device__ __forceinline__ void buffer_load_lds16(rsrc_t, char*, uint32_t, int) {}
+__device__ __forceinline__ void buffer_load_lds16_nt(rsrc_t, char*, uint32_t, int) {}
 #endif
 
 // Host: whether rows of ld 2-byte elements in the buffers at p0 and p1 (at
@@ -170,6 +177,7 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 struct TileRows {
   int e, v0, rows;
   int lo0, n0, lo1;  // chunk-0 first row and count; chunk-1 first row (0 if none)
+  int single;        // 1 if the tile holds all of its expert's rows (its only m-tile)
 
   // Row index of virtual row v on a split side: (buffer, row).
   __device__ __forceinline__ int split_row(int v, int* part) const {
@@ -283,7 +291,7 @@ struct MTileMap {
     }
     const uint64_t own = __ballot(lo <= local && local < hi);
     const int owner = __ffsll((unsigned long long)own) - 1;
-    int fe = 0, fv0 = 0, frows = 0, flo0 = 0, fn0 = 0, flo1 = 0;
+    int fe = 0, fv0 = 0, frows = 0, flo0 = 0, fn0 = 0, flo1 = 0, fsingle = 0;
     if (lane == owner) {
       int acc = lo;
       for (int e = e_begin; e < e_end; ++e) {
@@ -308,6 +316,7 @@ struct MTileMap {
           ++acc;
         }
         if (hit) {
+          fsingle = fv0 == 0 && frows == n;
           fe = e;
           flo0 = off0[e];
           fn0 = off0[e + 1] - flo0;
@@ -323,6 +332,7 @@ struct MTileMap {
     r.lo0 = __shfl(flo0, owner);
     r.n0 = __shfl(fn0, owner);
     r.lo1 = __shfl(flo1, owner);
+    r.single = __shfl(fsingle, owner);
     return r;
   }
 };
