@@ -200,6 +200,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
     if (col > a.N - 8) col = a.N - 8;
     b_src[t] = (const char*)(Be + (int64_t)k * a.N + col);
   }
+  // a weight panel that only this tile reads (its expert has one m-tile) is
+  // streamed with the non-temporal cache policy, as in the forward
+  const bool nt_b = __builtin_amdgcn_readfirstlane(tr.single) != 0;
   auto issue = [&](int kt, int buf) {
     char* base = smem + buf * STAGE;
 #pragma unroll
@@ -207,11 +210,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
       if (t < live_a)
         __builtin_amdgcn_global_load_lds((const void*)(a_src[t] + (int64_t)kt * 128),
                                          (lds_void*)(base + (wave * LA + t) * 1024), 16, 0, 0);
+    if (nt_b) {
 #pragma unroll
-    for (int t = 0; t < LB; ++t)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + (int64_t)kt * BK * a.N * 2),
-                                       (lds_void*)(base + A_BYTES + (wave * LB + t) * 1024), 16,
-                                       0, 0);
+      for (int t = 0; t < LB; ++t)
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + (int64_t)kt * BK * a.N * 2),
+                                         (lds_void*)(base + A_BYTES + (wave * LB + t) * 1024), 16,
+                                         0, 2);
+    } else {
+#pragma unroll
+      for (int t = 0; t < LB; ++t)
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[t] + (int64_t)kt * BK * a.N * 2),
+                                         (lds_void*)(base + A_BYTES + (wave * LB + t) * 1024), 16,
+                                         0, 0);
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -532,8 +543,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
         v.y = old.y + v.y;
         v.z = old.z + v.z;
         v.w = old.w + v.w;
+        *dst = v;
+      } else {
+        // written once here and read by nothing later in the layer: streamed
+        // (backward 1.44 -> 1.36 ms on the Zipf bench workload with the dgrad
+        // weight loads above, 22.4 -> 22.1 ms on the DeepSeek-V3-shaped one)
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(f32x4v{v.x, v.y, v.z, v.w}, (f32x4v*)dst);
       }
-      *dst = v;
     }
   }
 }
