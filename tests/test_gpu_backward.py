@@ -103,8 +103,10 @@ def check_weight_grads(L, ref, gwgu, gwd, tol, experts=None):
 FULL = [("tiny_f32", 1, None), ("tiny_f32", 3, None), ("t3_n4", 4, None),
         ("bf16_e64_zipf", 2, 256), ("odd_dims_bf16", 1, None), ("odd_dims_bf16", 3, None),
         ("odd_dims_f32", 4, None),
-        # full size, every output: 4096 tokens over 64 Zipf-skewed experts, a chunk pair
-        ("bf16_e64_zipf", 2, None)]
+        # full size, every output: 4096 tokens over 64 Zipf-skewed experts, a chunk pair;
+        # 1000 tokens all routed to experts {0, 1} (the other 254 experts' gradients zero);
+        # the packed 16k-token layer at N=2
+        ("bf16_e64_zipf", 2, None), ("skew_two_experts", 1, None), ("packed16k_e128", 2, None)]
 
 
 @pytest.mark.timeout(900)
