@@ -212,3 +212,23 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         moe.moe_permute(shape, 0, torch.zeros(4, 128), torch.zeros(8, dtype=torch.int32),
                         torch.zeros(8, 128))
+
+
+def test_noalloc_refuses_oversized_shapes_before_any_hip_call():
+    """moe_chunked_forward_noalloc checks the shape's workspace against its 64 MiB
+    static scratch on the host, before looking the scratch up on a device or
+    enqueuing anything, so the refusal needs no GPU; a bad shape is refused as
+    by the other entry points."""
+    fake = 0x10000000  # never dereferenced
+    big = moe.make_shape(65536, 64, 4, 8, 64, 1, 1, "bf16")  # about 138 MB of workspace
+    assert moe.moe_workspace_size(big) > 64 << 20
+    assert _raw("moe_chunked_forward_noalloc", ctypes.byref(big), fake, fake, fake, fake, fake,
+                fake, None, None) == 3  # MOE_ERR_WORKSPACE_TOO_SMALL
+    dsv3 = moe.make_shape(4096, 7168, 256, 8, 2048, 16, 1, "bf16")  # 604 MB
+    assert _raw("moe_chunked_forward_noalloc", ctypes.byref(dsv3), fake, fake, fake, fake, fake,
+                fake, None, None) == 3
+    bad = moe.make_shape(64, 96, 256, 8, 2048, 16, 1, "bf16")  # H not a multiple of 64
+    assert _raw("moe_chunked_forward_noalloc", ctypes.byref(bad), fake, fake, fake, fake, fake,
+                fake, None, None) == 2  # MOE_ERR_UNSUPPORTED
+    # a decode-sized batch fits the scratch
+    assert moe.moe_workspace_size(moe.make_shape(64, 7168, 256, 8, 2048, 16, 1, "bf16")) <= 64 << 20
