@@ -388,6 +388,37 @@ def chunk_sweep(moe, torch, synth, name, Ns, steps):
     return res
 
 
+def vendor_dense_gemm(torch, reps=20):
+    """Context for the matrix-core fractions: the vendor library's dense bf16 GEMM
+    (torch.matmul on contiguous 2-D operands, hipBLASLt underneath) on the shapes
+    of the MFMA-bound expert launches, one expert's worth: the two-expert skew's
+    gate/up (4000 x 7168 by 7168 x 4096) and down (4000 x 2048 by 2048 x 7168),
+    and a dense 16384 x 2048 by 2048 x 1536 (the packed 16k-token gate/up if all
+    rows went to one expert).  Not on the layer's path."""
+    res = {}
+    for name, (m, kk, n) in {"skew_gate_up_one_expert": (4000, 7168, 4096),
+                             "skew_down_one_expert": (4000, 2048, 7168),
+                             "packed16k_gate_up_dense": (16384, 2048, 1536)}.items():
+        a = torch.randn(m, kk, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(kk, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        flop = 2.0 * m * kk * n
+        res[name] = {"m": m, "k": kk, "n": n, "us": sec * 1e6, "TFLOPs": flop / sec / 1e12,
+                     "mfma_frac": flop / sec / MFMA_PEAK["bf16"]}
+        del a, b
+    return res
+
+
 def prefetch_ab(moe, torch, synth, name, base_cfg, base_inp, rounds=3, steps=20):
     """The pair-fused schedule with and without the weight warm-up on a second
     stream (MOE_SCHEDULE_PAIR_FUSED_PREFETCH), interleaved over `rounds`, on one
@@ -571,6 +602,8 @@ def main():
         "expert_load": {"max_over_mean": float(inp["counts"].max() / inp["counts"].mean()),
                         "empty_experts": int((inp["counts"] == 0).sum())},
     }
+    log("vendor dense GEMM reference")
+    line["vendor_dense_gemm_bf16"] = vendor_dense_gemm(torch)
     if not args.no_prefetch_ab:
         log("prefetch schedule A/B")
         line["prefetch_schedule_ab"] = [prefetch_ab(moe, torch, synth, n, cfg, inp)
