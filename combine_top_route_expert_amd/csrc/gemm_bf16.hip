@@ -181,21 +181,31 @@ struct TileLoader {
     mrows = tr.rows;
     const int row_in_blk = lane / G::CH, slot = lane % G::CH;
     live_a = 0;
+    int rr[LA], ch[LA];
 #pragma unroll
     for (int t = 0; t < LA; ++t) {
       const int row = (wave * LA + t) * G::RPB + row_in_blk;
-      const int chunk = slot ^ G::swz(row);
-      const int r = row < mrows ? row : mrows - 1;
-      if (a.gather[0]) {
-        // permute fused into the row addressing: chunk row -> token
-        int part;
-        const int cr = tr.split_row(tr.v0 + r, &part);
-        const int32_t* src = part ? a.gather[1] : a.gather[0];
-        a_src[t] = (const char*)(a.A[0] + (int64_t)(src[cr] / a.gather_k) * a.K + chunk * 8);
-      } else {
-        a_src[t] = (const char*)(row_ptr(a.A, a.a_split, tr, tr.v0 + r, a.K) + chunk * 8);
-      }
+      ch[t] = slot ^ G::swz(row);
+      rr[t] = row < mrows ? row : mrows - 1;
       live_a += (wave * LA + t) * G::RPB < mrows ? 1 : 0;
+    }
+    if (a.gather[0]) {
+      // permute fused into the row addressing: chunk row -> token (the LA
+      // lookups are issued together and waited for once)
+      int src[LA];
+#pragma unroll
+      for (int t = 0; t < LA; ++t) {
+        int part;
+        const int cr = tr.split_row(tr.v0 + rr[t], &part);
+        src[t] = (part ? a.gather[1] : a.gather[0])[cr];
+      }
+#pragma unroll
+      for (int t = 0; t < LA; ++t)
+        a_src[t] = (const char*)(a.A[0] + (int64_t)(src[t] / a.gather_k) * a.K + ch[t] * 8);
+    } else {
+#pragma unroll
+      for (int t = 0; t < LA; ++t)
+        a_src[t] = (const char*)(row_ptr(a.A, a.a_split, tr, tr.v0 + rr[t], a.K) + ch[t] * 8);
     }
     // the expert is the same for the whole workgroup: keep its base scalar
     const int e = __builtin_amdgcn_readfirstlane(tr.e);
@@ -305,18 +315,19 @@ __device__ __forceinline__ void wait_loads(int n) {
 
 // Epilogue through LDS.  MFMA 32x32 output: lane l holds column l % 32 of
 // rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of each block.  Every wave writes
-// its blocks (after SwiGLU for gate_up) as bf16 into a row-major C tile in the
-// freed stage buffers, then the workgroup stores the tile 16 bytes per lane,
-// one row segment at a time.  (Storing each lane's 2-byte elements straight
-// from the MFMA layout took one guarded global store per element.)  Chunk ch
-// (8 elements) of tile row r sits at chunk ch ^ 4((r/4) mod 2), so that the
-// two rows a 2-byte LDS write covers (r and r + 4) fall in different banks.
-// Same values, same bits.  PLANES = 3 (gate_up in the backward's recompute)
-// also saves g and u into the joint [rows][2I] copy: one plane per pass.
+// its nblk 32-row blocks from row row0 (after SwiGLU for gate_up) as bf16 into a
+// row-major C tile in the freed stage buffers, then the workgroup stores the
+// tile 16 bytes per lane, one row segment at a time.  (Storing each lane's
+// 2-byte elements straight from the MFMA layout took one guarded global store
+// per element.)  Chunk ch (8 elements) of tile row r sits at chunk
+// ch ^ 4((r/4) mod 2), so that the two rows a 2-byte LDS write covers (r and
+// r + 4) fall in different banks.  Same values, same bits.  PLANES = 3
+// (gate_up in the backward's recompute) also saves g and u into the joint
+// [rows][2I] copy: one plane per pass.
 template <bool kGateUp, int PLANES, int FM, int FN, int BM, int BN, int WM, int WN, int NT>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
-                                               const TileRows& tr, int nt, int wm, int wn,
-                                               int lane, char* smem) {
+                                               const TileRows& tr, int nt, int row0, int nblk,
+                                               int wn, int lane, char* smem) {
   constexpr int CT = kGateUp ? BN / 2 : BN;  // tile columns of C
   constexpr int CPR = CT / 8;                // 16-byte chunks per tile row
   static_assert(CPR >= 8, "chunk swizzle needs 8 chunks per row");
@@ -324,7 +335,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
   auto lds_at = [](int r, int c) {
     return r * (CT * 2) + ((((c >> 3) ^ (((r >> 2) & 1) << 2))) << 4) + (c & 7) * 2;
   };
-  const int rbase = wm * WM + 4 * (lane >> 5);
+  const int rbase = row0 + 4 * (lane >> 5);
   const int col0 = nt * CT;
   const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
 #pragma unroll
@@ -332,7 +343,8 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
     if (plane > 0) __syncthreads();  // the previous plane's reads are done
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      if (wm * WM + i * 32 >= tr.rows) break;  // blocks past the tile's rows: never stored
+      // blocks past the wave's band or the tile's rows: never stored
+      if (i >= nblk || row0 + i * 32 >= tr.rows) break;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
@@ -433,17 +445,92 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
   }
 }
 
+// K loop of a tile on the wide path: the first STAGES - 1 stages, then
+// k_loop over the 32-row blocks of this wave's band that hold rows of the
+// tile.  Blocks past them feed only outputs that are never stored, so a wide
+// tile skips their MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block
+// loop, 3 runs the full one).  A one-block band always runs its MFMAs: a
+// wave-uniform branch there measured slower than the wasted work.
+template <int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, bool kNt, class Loader>
+__device__ __forceinline__ void wide_k(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem, int KT,
+                                       int per_stage, int lane, int wm, int wn, int rows) {
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) ld.template issue<kNt>(smem, s, s);
+  const int band_rows = rows - wm * WM;
+  const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
+#define MOE_K_LOOP(F) \
+  k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
+  if constexpr (FM == 1) {
+    MOE_K_LOOP(1);
+  } else {
+    if (fm_live > 2)
+      MOE_K_LOOP(FM);
+    else if (fm_live == 2)
+      MOE_K_LOOP(2);
+    else if (fm_live == 1)
+      MOE_K_LOOP(1);
+    else
+      MOE_K_LOOP(0);
+  }
+#undef MOE_K_LOOP
+}
+
+// Row split of a compact tile (at most 32, 64, 128 or 160 rows) between the
+// two wave rows: wave row 0 takes 32-row blocks 0..f0-1, wave row 1 the next
+// f1.  A tile that holds its expert's whole row block (a weight-streaming tile)
+// spreads its rows over both wave rows, so both waves on a SIMD run MFMAs and
+// each hides the other's fragment reads (DeepSeek-V3-shaped gate/up: one wave
+// per SIMD holding all of a 128-row tile's MFMAs ran them at about half the
+// matrix rate; the layer 4.59 -> 4.48 ms).  The tail tile of a larger expert
+// keeps them on wave row 0 (spreading them there measured 1-3% slower on the
+// MFMA-bound launches).
+constexpr int compact_f0(int rows, bool spread) {
+  return spread ? (rows <= 64 ? 1 : rows <= 128 ? 2 : 3) : (rows <= 32 ? 1 : rows <= 64 ? 2 : 4);
+}
+constexpr int compact_f1(int rows, bool spread) {
+  return spread ? (rows <= 32 ? 0 : rows <= 64 ? 1 : 2) : (rows <= 128 ? 0 : 1);
+}
+
+// MFMAs of one compact stage at sa (rows of A, then B): the wave's F 32-row
+// blocks from row0 against its FN 32-column blocks, the fragments of each
+// 16-deep sub-step read right before its MFMAs.
+template <int F, int SROWS, int FM, int FN, int WN, int BK, class Loader>
+__device__ __forceinline__ void compact_mfma(f32x16 (&acc)[FM][FN], const char* sa, int lane,
+                                             int wn, int row0) {
+  using G = StageGeom<BK>;
+  static_assert(F <= FM, "band blocks");
+  if constexpr (F > 0) {
+    const char* sb = sa + Loader::template small_a<SROWS>();
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int fo = G::frag_offset(lane, kk);
+      bf16x8 af[F], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+        af[i] = *(const bf16x8*)(sa + (row0 + i * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
 // The K loop of a tile with at most SROWS (32, 64, 128 or 160) rows: such a
 // tile (a small expert's only m-tile) is bound by streaming its B panel rather
 // than by MFMAs, so it uses the compact stage layout and SSTAGES stages
 // (SSTAGES - 1 in flight) to keep more weight bytes in flight.  The wave holds
 // F 32-row blocks of the tile's rows starting at row0 (its band); a wave with
-// F = 0 only loads and joins the barriers.
+// F = 0 only loads and joins the barriers.  (Reading the next sub-step's
+// fragments during the current MFMAs, as k_loop does, measured no faster here.)
 template <int F, int SROWS, int SSTAGES, int FM, int FN, int WN, int BK, bool kNt, class Loader>
 __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
                                              int KT, int per_stage, int lane, int wn, int row0) {
-  using G = StageGeom<BK>;
-  constexpr bool kMfma = F > 0;
   constexpr int STAGE = Loader::template small_stage<SROWS>();
 #pragma unroll
   for (int s = 0; s < SSTAGES - 1; ++s)
@@ -454,26 +541,8 @@ __device__ __forceinline__ void k_loop_small(f32x16 (&acc)[FM][FN], const Loader
     __builtin_amdgcn_s_barrier();
     if (kt + SSTAGES - 1 < KT)
       ld.template issue_small<SROWS, kNt>(smem, kt + SSTAGES - 1, (kt + SSTAGES - 1) % SSTAGES);
-    if constexpr (kMfma) {
-      const char* sa = smem + (kt % SSTAGES) * STAGE;
-      const char* sb = sa + Loader::template small_a<SROWS>();
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int fo = G::frag_offset(lane, kk);
-        bf16x8 af[F > 0 ? F : 1], bfr[FN];
-#pragma unroll
-        for (int i = 0; i < F; ++i)
-          af[i] = *(const bf16x8*)(sa + (row0 + i * 32) * G::ROW_BYTES + fo);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
-#pragma unroll
-        for (int i = 0; i < F; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-    }
+    compact_mfma<F, SROWS, FM, FN, WN, BK, Loader>(acc, smem + (kt % SSTAGES) * STAGE, lane, wn,
+                                                   row0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   }
 }
@@ -540,45 +609,34 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     // of one expert stay cached (non-temporal there cost the two-expert skew 13%).
     auto run_k = [&](auto nt_tag) __attribute__((always_inline)) {
     constexpr bool kNt = decltype(nt_tag)::value;
-#define MOE_K_SMALL(F, SR) \
-  k_loop_small<F, SR, 3, FM, FN, WN, BK, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wn, wm * WM)
-    if (kSmallPath && tr.rows <= 32) {
-      if (wm == 0) MOE_K_SMALL(1, 32); else MOE_K_SMALL(0, 32);
-    } else if (kSmallPath && tr.rows <= 64) {
-      if (wm == 0) MOE_K_SMALL(2, 64); else MOE_K_SMALL(0, 64);
-    } else if (kSmallPath && tr.rows <= 128) {
-      if (wm == 0) MOE_K_SMALL(4, 128); else MOE_K_SMALL(0, 128);
-    } else if (kSmallPath && tr.rows <= 160) {
-      // the second wave row holds rows 128..159: one block
-      if (wm == 0) MOE_K_SMALL(4, 160); else MOE_K_SMALL(1, 160);
-    } else {
-#undef MOE_K_SMALL
-#pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
-        if (s < KT) ld.template issue<kNt>(smem, s, s);
-      // 32-row blocks of this wave's band that hold rows of the tile.  Blocks past
-      // them feed only outputs that are never stored, so a wide tile skips their
-      // MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block loop, 3 runs
-      // the full one).  A one-block band always runs its MFMAs: a wave-uniform
-      // branch there measured slower than the wasted work.
-      const int band_rows = tr.rows - wm * WM;
-      const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
-#define MOE_K_LOOP(F) \
-      k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
-      if constexpr (FM == 1) {
-        MOE_K_LOOP(1);
-      } else {
-        if (fm_live > 2)
-          MOE_K_LOOP(FM);
-        else if (fm_live == 2)
-          MOE_K_LOOP(2);
-        else if (fm_live == 1)
-          MOE_K_LOOP(1);
-        else
-          MOE_K_LOOP(0);
-      }
-#undef MOE_K_LOOP
+#define MOE_K_SMALL(SR)                                                                          \
+  do {                                                                                           \
+    constexpr int F0 = compact_f0(SR, kNt), F1 = compact_f1(SR, kNt);                            \
+    if (wm == 0)                                                                                 \
+      k_loop_small<F0, SR, 3, FM, FN, WN, BK, kNt, Loader>(acc, ld, smem, KT, per_stage, lane,   \
+                                                           wn, 0);                               \
+    else                                                                                         \
+      k_loop_small<F1, SR, 3, FM, FN, WN, BK, kNt, Loader>(acc, ld, smem, KT, per_stage, lane,   \
+                                                           wn, F0 * 32);                         \
+  } while (0)
+    bool compact = false;
+    if constexpr (kSmallPath) {
+      compact = true;
+      if (tr.rows <= 32)
+        MOE_K_SMALL(32);
+      else if (tr.rows <= 64)
+        MOE_K_SMALL(64);
+      else if (tr.rows <= 128)
+        MOE_K_SMALL(128);
+      else if (tr.rows <= 160)
+        MOE_K_SMALL(160);
+      else
+        compact = false;
     }
+#undef MOE_K_SMALL
+    if (!compact)
+      wide_k<FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn,
+                                                          tr.rows);
     };
     if (tr.single)
       run_k(std::true_type{});
@@ -587,8 +645,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     static_assert(BM * (kGateUp ? BN / 2 : BN) * 2 <= STAGES * Loader::STAGE_BYTES,
                   "C tile fits the stage buffers");
     __syncthreads();  // every wave is done with the stage buffers
-    store_tile_lds<kGateUp, kSaveGU ? 3 : 1, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, wm, wn,
-                                                                             lane, smem);
+    // this wave's rows: its wave row's WM on the wide path, the compact split
+    // (recomputed here so that nothing more stays live across the K loop)
+    int band0 = wm * WM, nblk = FM;
+    if constexpr (kSmallPath) {
+      if (tr.rows <= 160) {
+        const bool spread = tr.single != 0;
+        const int f0 = compact_f0(tr.rows, spread);
+        band0 = wm * f0 * 32;
+        nblk = wm == 0 ? f0 : compact_f1(tr.rows, spread);
+      }
+    }
+    store_tile_lds<kGateUp, kSaveGU ? 3 : 1, FM, FN, BM, BN, WM, WN, 64 * NW>(a, acc, tr, nt, band0,
+                                                                             nblk, wn, lane, smem);
     if constexpr (!kLoop) break;
     __syncthreads();  // the C tile has left LDS before the next tile's stage loads
   }
