@@ -25,12 +25,14 @@ __all__ = [
     "moe_chunked_forward_schedule", "moe_backward_workspace_size", "moe_chunked_backward",
     "moe_unpermute_combine_backward", "moe_permute_backward", "MOE_F32", "MOE_BF16",
     "MOE_SCHEDULE_PAIR_FUSED", "MOE_SCHEDULE_PER_CHUNK", "MOE_SCHEDULE_PAIR_FUSED_PREFETCH",
+    "MOE_SCHEDULE_EXPERT_HALVES",
     "EXPORTED_SYMBOLS",
     "moe_chunked_forward_noalloc",
 ]
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCHEDULE_PAIR_FUSED, MOE_SCHEDULE_PER_CHUNK, MOE_SCHEDULE_PAIR_FUSED_PREFETCH = 0, 1, 2
+MOE_SCHEDULE_EXPERT_HALVES = 3
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 

@@ -725,7 +725,7 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
   moe_status st = resolve_shape(shape, &s);
   if (st != MOE_OK) return st;
   if (schedule != MOE_SCHEDULE_PAIR_FUSED && schedule != MOE_SCHEDULE_PER_CHUNK &&
-      schedule != MOE_SCHEDULE_PAIR_FUSED_PREFETCH)
+      schedule != MOE_SCHEDULE_PAIR_FUSED_PREFETCH && schedule != MOE_SCHEDULE_EXPERT_HALVES)
     return MOE_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   if (!aligned(dev_error, 4)) return MOE_ERR_INVALID_ARG;
@@ -777,6 +777,15 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
     if (he == hipSuccess) he = join(s1, s0, ev[0]);  // s1 starts after the metadata
     if (he != hipSuccess) return MOE_ERR_HIP;
   }
+  // the expert-halves schedule: each pair's expert GEMMs in two launches over
+  // experts [0, E/2) and [E/2, E), the first half's down on s1 beside the second
+  // half's gate_up on s0
+  const bool halves = schedule == MOE_SCHEDULE_EXPERT_HALVES && s1 != nullptr && s1 != s0 &&
+                      s.E >= 2;
+  if (halves) {
+    he = thread_events(ev);
+    if (he != hipSuccess) return MOE_ERR_HIP;
+  }
   bool used_s1 = false;
   auto chunk_rows = [&](int c, int* t0, int* t1) {
     *t0 = *t1 = 0;
@@ -809,8 +818,6 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
       io.gather[1] = src_row + (size_t)u0 * s.k;
       io.gather_k = s.k;
       io.c[0] = w + p.slot_act[0];
-      st = gate_up(s, io, w_gate_up, s0);
-      if (st != MOE_OK) return st;
       GroupedIO dn{};
       dn.off[0] = io.off[0];
       dn.off[1] = io.off[1];
@@ -819,8 +826,40 @@ moe_status moe_chunked_forward_schedule(const moe_shape* shape, const void* hidd
       dn.c[0] = xy0;
       dn.c[1] = xy1;
       dn.c_split = true;
-      st = down(s, dn, w_down, s0);
-      if (st != MOE_OK) return st;
+      if (!halves) {
+        st = gate_up(s, io, w_gate_up, s0);
+        if (st != MOE_OK) return st;
+        st = down(s, dn, w_down, s0);
+        if (st != MOE_OK) return st;
+      } else {
+        // Experts [e0, e1) of the same launches: the offsets from e0 on, the
+        // weights of expert e0 on (every row index stays absolute).  The halves
+        // touch disjoint rows of act and y, so only each half's gate_up -> down
+        // order matters; the row bound stays the pair's.
+        auto part = [&](const GroupedIO& g, int e0) {
+          GroupedIO h = g;
+          h.off[0] = g.off[0] + e0;
+          h.off[1] = g.off[1] ? g.off[1] + e0 : nullptr;
+          return h;
+        };
+        const int eh = s.E / 2;
+        Shape sa = s, sb = s;
+        sa.E = eh;
+        sb.E = s.E - eh;
+        const char* wgu1 = (const char*)w_gate_up + (size_t)eh * 2 * s.I * s.H * s.elem;
+        const char* wd1 = (const char*)w_down + (size_t)eh * s.H * s.I * s.elem;
+        st = gate_up(sa, part(io, 0), w_gate_up, s0);
+        if (st != MOE_OK) return st;
+        if (join(s1, s0, ev[0]) != hipSuccess) return MOE_ERR_HIP;  // first half's act ready
+        st = down(sa, part(dn, 0), w_down, s1);
+        if (st != MOE_OK) return st;
+        used_s1 = true;
+        st = gate_up(sb, part(io, eh), wgu1, s0);
+        if (st != MOE_OK) return st;
+        st = down(sb, part(dn, eh), wd1, s0);
+        if (st != MOE_OK) return st;
+        if (join(s0, s1, ev[1]) != hipSuccess) return MOE_ERR_HIP;  // first half's y ready
+      }
       he = rows1 > 0 ? launch_combine_pair(s, t0, u0, u1, xy0, xy1, dst_row, top_k_weights,
                                            out, s0)
                      : launch_combine(s, t0, t1, xy0, dst_row, top_k_weights, out, s0);

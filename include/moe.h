@@ -79,7 +79,8 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_schedule {
   MOE_SCHEDULE_PAIR_FUSED = 0,  /* one expert-GEMM launch pair per chunk pair (default) */
   MOE_SCHEDULE_PER_CHUNK = 1,   /* every chunk runs all four steps on its own stream */
-  MOE_SCHEDULE_PAIR_FUSED_PREFETCH = 2  /* pair-fused, plus a weight warm-up on s1 */
+  MOE_SCHEDULE_PAIR_FUSED_PREFETCH = 2,  /* pair-fused, plus a weight warm-up on s1 */
+  MOE_SCHEDULE_EXPERT_HALVES = 3  /* pair-fused, each expert GEMM split over two expert halves */
 } moe_schedule;
 
 /* Problem shape.  Field names follow the pages' notation. */
@@ -288,6 +289,13 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  *    dual-stream article, "02 Weight預取雙流並行": weights prefetched on a second
  *    stream while the first is busy).  Same bits; without a distinct s1 it is the
  *    pair-fused schedule.
+ *  MOE_SCHEDULE_EXPERT_HALVES: the pair-fused schedule with each expert GEMM
+ *    launched twice, over experts [0, E/2) and [E/2, E): the first half's down on
+ *    s1 runs beside the second half's gate_up on s0, so each launch's last,
+ *    partly idle moments overlap the other's work (two micro-batches on two
+ *    streams, as the Ascend dual-stream article's "01 Prefill micro-batch雙流並行"
+ *    splits the work, here by experts, so that no weight is read twice).  Same
+ *    bits; without a distinct s1 it is the pair-fused schedule.
  * s1 == s0 (or null) is legal and gives the same bits without overlap; the
  * result never depends on N or on the schedule.  On return s0 is ordered after
  * all work of the call.  ws must hold moe_workspace_size bytes.  dev_error is

@@ -337,7 +337,7 @@ def test_chunked_equals_unchunked_bitwise(name, Ns):
     base, _ = run_forward(L, L.shape(1), two_streams=False)
     for N in Ns:
         for sched in (moe.MOE_SCHEDULE_PAIR_FUSED, moe.MOE_SCHEDULE_PER_CHUNK,
-                      moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH):
+                      moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH, moe.MOE_SCHEDULE_EXPERT_HALVES):
             for two in (True, False):
                 say(f"chunked {name} N={N} schedule={sched} two_streams={two}")
                 out, _ = run_forward(L, L.shape(N), two_streams=two, schedule=sched)
@@ -356,6 +356,28 @@ def test_prefetch_schedule_same_bits_and_oracle(name, N):
     say(f"prefetch schedule {name} N={N}: prefetch on s1")
     out, err = run_forward(L, L.shape(N), two_streams=True,
                            schedule=moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH)
+    assert err == 0
+    assert torch.equal(out, base)
+    toks = sample_tokens(cfg.T, 16)
+    ref = oracle.moe_tokens(toks, L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I)
+    e = oracle.row_rel_err(f64(out[toks]), ref)
+    assert e <= TOL[cfg.dtype], e
+
+
+@pytest.mark.parametrize("name,N", [("dsv3_e256", 1), ("decode_t64", 1), ("bf16_e64_zipf", 2),
+                                    ("skew_two_experts", 1), ("odd_dims_f32", 3)])
+def test_expert_halves_schedule_same_bits_and_oracle(name, N):
+    """The expert-halves schedule (each expert GEMM launched over experts
+    [0, E/2) and [E/2, E), the first half's down on s1 beside the second half's
+    gate_up on s0) gives the bits of the default schedule, and sampled tokens
+    match the oracle."""
+    L = layer_for(name)
+    cfg = L.cfg
+    say(f"expert halves {name} N={N}: default")
+    base, _ = run_forward(L, L.shape(N), two_streams=False)
+    say(f"expert halves {name} N={N}: halves on s0 and s1")
+    out, err = run_forward(L, L.shape(N), two_streams=True,
+                           schedule=moe.MOE_SCHEDULE_EXPERT_HALVES)
     assert err == 0
     assert torch.equal(out, base)
     toks = sample_tokens(cfg.T, 16)

@@ -183,7 +183,7 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                 None) == 1
     assert _raw("moe_permute_backward", sp, 0, fake + 4, fake, fake, None) == 1
     # unknown schedule
-    for sched in (-1, 3):
+    for sched in (-1, 4):
         assert _raw("moe_chunked_forward_schedule", sp, fake, fake, fake, fake, fake, fake, None,
                     fake, need, None, None, sched) == 1
 
