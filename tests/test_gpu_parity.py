@@ -269,6 +269,43 @@ def test_forward_every_row_vs_oracle(name, N, T):
     assert e <= TOL[cfg.dtype], e
 
 
+def _routing_with_counts(counts, T, k, seed=5):
+    """top_k_index whose expert e receives counts[e] of the T * k slots, every
+    token's k experts distinct (the slots sorted by expert, filled column by
+    column: a run of at most T equal ids never lands twice in one token)."""
+    assert sum(counts) == T * k and max(counts) <= T
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    idx = ids.reshape(k, T).T.copy()
+    rng = np.random.default_rng(seed)
+    idx = idx[rng.permutation(T)]  # tokens in random order, counts unchanged
+    assert all(len(set(r)) == k for r in idx.tolist())
+    return idx
+
+
+@pytest.mark.parametrize("N", [1, 2])
+def test_compact_tile_row_classes_every_row(N):
+    """Experts at every row count around the compact tiles' class bounds (1,
+    31-33, 63-65, 127-129, 159-161; a single-tile expert's rows split over both
+    wave rows) and around one wide tile (255-257), and larger experts whose last
+    m-tile falls in each class (276, 306, 356, 406, 456, 641 rows: tails of 20,
+    50, 100, 150, 200, 129 rows on one wave row), in a launch large enough for
+    the 256 x 256 instance (5200 rows).  Every output row against the oracle."""
+    counts = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 159, 160, 161, 255, 256, 257,
+              276, 306, 356, 406, 456, 641, 200, 200, 200, 200, 38, 0, 0, 0]
+    T, k = 650, 8
+    cfg = C["bf16_e64_zipf"].with_(T=T, E=len(counts), k=k, H=512, I=256)
+    idx = _routing_with_counts(counts, T, k)
+    _, w = synth.routing(cfg)
+    L = build_layer(cfg, idx, w)
+    say(f"compact row classes N={N}")
+    out, err = run_forward(L, L.shape(N))
+    ref, meta = oracle.moe_forward(L.hidden64(), idx, w, L.expert64, cfg.E, cfg.I, 1, N)
+    assert err == meta["n_invalid"] == 0
+    np.testing.assert_array_equal(meta["counts"].sum(axis=0), counts)
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL["bf16"], e
+
+
 @pytest.mark.parametrize("name,kw", [
     ("odd_dims_bf16", dict(T=50, k=64, E=96, H=128, I=128, groups=2)),
     ("odd_dims_f32", dict(T=29, k=64, E=70, H=36, I=20, groups=1)),
