@@ -476,22 +476,6 @@ __device__ __forceinline__ void wide_k(f32x16 (&acc)[FM][FN], const Loader& ld, 
 #undef MOE_K_LOOP
 }
 
-// Row split of a compact tile (at most 32, 64, 128 or 160 rows) between the
-// two wave rows: wave row 0 takes 32-row blocks 0..f0-1, wave row 1 the next
-// f1.  A tile that holds its expert's whole row block (a weight-streaming tile)
-// spreads its rows over both wave rows, so both waves on a SIMD run MFMAs and
-// each hides the other's fragment reads (DeepSeek-V3-shaped gate/up: one wave
-// per SIMD holding all of a 128-row tile's MFMAs ran them at about half the
-// matrix rate; the layer 4.59 -> 4.48 ms).  The tail tile of a larger expert
-// keeps them on wave row 0 (spreading them there measured 1-3% slower on the
-// MFMA-bound launches).
-constexpr int compact_f0(int rows, bool spread) {
-  return spread ? (rows <= 64 ? 1 : rows <= 128 ? 2 : 3) : (rows <= 32 ? 1 : rows <= 64 ? 2 : 4);
-}
-constexpr int compact_f1(int rows, bool spread) {
-  return spread ? (rows <= 32 ? 0 : rows <= 64 ? 1 : 2) : (rows <= 128 ? 0 : 1);
-}
-
 // MFMAs of one compact stage at sa (rows of A, then B): the wave's F 32-row
 // blocks from row0 against its FN 32-column blocks, the fragments of each
 // 16-deep sub-step read right before its MFMAs.

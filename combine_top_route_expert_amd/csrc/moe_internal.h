@@ -337,6 +337,24 @@ struct MTileMap {
   }
 };
 
+// Row split of a compact tile (at most 32, 64, 128 or 160 rows) of the 256 x 256
+// grouped GEMM between its two wave rows: wave row 0 takes 32-row blocks
+// 0 .. f0-1, wave row 1 the next f1 (rows is the tile's row count, or the
+// bound of its class: both give the same split).  A tile that holds its
+// expert's whole row block (a weight-streaming tile) spreads its rows over
+// both wave rows, so both waves on a SIMD run MFMAs and each hides the other's
+// fragment reads (DeepSeek-V3-shaped gate/up: one wave per SIMD holding all of
+// a 128-row tile's MFMAs ran them at about half the matrix rate; the layer
+// 4.59 -> 4.48 ms).  The tail tile of a larger expert keeps them on wave row 0
+// (spreading them there measured 1-3% slower on the MFMA-bound launches).
+// Also compiled for the host, where its coverage is checked.
+__host__ __device__ constexpr int compact_f0(int rows, bool spread) {
+  return spread ? (rows <= 64 ? 1 : rows <= 128 ? 2 : 3) : (rows <= 32 ? 1 : rows <= 64 ? 2 : 4);
+}
+__host__ __device__ constexpr int compact_f1(int rows, bool spread) {
+  return spread ? (rows <= 32 ? 0 : rows <= 64 ? 1 : 2) : (rows <= 128 ? 0 : 1);
+}
+
 // Workgroup -> (m-tile, n-tile) for an MTileMap.  Workgroup b runs on XCD
 // b % 8 (checked against the hardware XCC id), and an XCD starts its
 // workgroups in order of b.  Which m-tiles an XCD gets: a contiguous range of

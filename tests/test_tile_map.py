@@ -2,7 +2,9 @@
 (m-tile, n-tile) map, compiled for the CPU from the library's own header, must
 cover every tile exactly once, keep each XCD's valid positions a prefix, give
 no XCD more than ceil(total/8) m-tiles, keep large m-tiles contiguous per XCD
-and put the reserved smallest tiles last.  No GPU needed."""
+and put the reserved smallest tiles last; the compact tiles' row split between
+the two wave rows must cover every row within the stage and the accumulators.
+No GPU needed."""
 import os
 import shutil
 import subprocess

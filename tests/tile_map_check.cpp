@@ -12,6 +12,13 @@
 //   5. each XCD's large m-tiles are one contiguous, increasing range;
 //   6. an XCD's last min(reserve, small) positions hold its highest-numbered
 //      (smallest) small m-tiles, in increasing order.
+// And the compact tiles' row split between the two wave rows (compact_f0 /
+// compact_f1 in the same header), for every row count 1..160 and both forms:
+//   7. the split of a tile's row count equals the split of its class bound (the
+//      K loop is chosen by class, the epilogue by row count);
+//   8. the two bands cover every row: 32 * (f0 + f1) >= rows;
+//   9. they stay within the compact stage's rows, 32 * (f0 + f1) <= class bound,
+//      and within a wave's 4 accumulator blocks; wave row 0 holds at least one.
 // Prints one line per failing case and exits non-zero if any failed.
 //
 //   check [seed] [random_cases]
@@ -87,6 +94,19 @@ void check_case(int large, int total, int n_tiles, int reserve) {
     }
 }
 
+void check_compact_split() {
+  for (int spread = 0; spread < 2; ++spread)
+    for (int rows = 1; rows <= 160; ++rows) {
+      const int cls = rows <= 32 ? 32 : rows <= 64 ? 64 : rows <= 128 ? 128 : 160;
+      const int f0 = moe::compact_f0(rows, spread), f1 = moe::compact_f1(rows, spread);
+      const bool ok = f0 == moe::compact_f0(cls, spread) && f1 == moe::compact_f1(cls, spread) &&
+                      32 * (f0 + f1) >= rows && 32 * (f0 + f1) <= cls && f0 >= 1 && f0 <= 4 &&
+                      f1 >= 0 && f1 <= 4;
+      if (!ok && ++fails <= 20)
+        std::printf("FAIL compact split: rows=%d spread=%d f0=%d f1=%d\n", rows, spread, f0, f1);
+    }
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -125,6 +145,8 @@ int main(int argc, char** argv) {
     check_case(0, total, 1, 32);
     cases += 3;
   }
+  check_compact_split();
+  cases += 320;
   std::printf("%d cases, %d failures\n", cases, fails);
   return fails ? 1 : 0;
 }
