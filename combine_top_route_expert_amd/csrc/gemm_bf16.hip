@@ -57,7 +57,16 @@
 // stages, two in flight (k_loop_small): 41 -> 33 us per gate/up tile of at most
 // 32 rows on the Zipf workload; the 160-row case (three 52 KB stages, 156 KB of
 // LDS) took the DeepSeek-V3-shaped layer, whose experts hold 95-160 rows, from
-// 4.89 to 4.79 ms (down 1724 -> 1683 us).
+// 4.89 to 4.79 ms (down 1724 -> 1683 us).  When such a tile holds all of its
+// expert's rows its 32-row blocks are split between the two wave rows
+// (compact_f0 / compact_f1), so that both waves on each SIMD run MFMAs.
+//
+// Also measured and dropped, on these launches: a persistent form (one
+// workgroup per CU taking its XCD's tiles in sequence, the next tile's first
+// stages loaded during the current tile's last steps), for weight-streaming
+// and for MFMA-bound launches; two workgroups per CU with 32-deep stages; K
+// stages rotated per expert.  The hardware's dynamic dispatch of one-tile
+// workgroups balances the tiles better than any fixed sequence per CU.
 //
 // What bounds it (measured with per-workgroup timestamps): the MFMA loop alone
 // (no global loads) runs at ~94% of the matrix peak at the clock it gets, and
