@@ -15,7 +15,8 @@
 // Pipeline: K advances BK (64) at a time.  Each stage of the A (rows) and B
 // (weight) tiles is copied HBM -> LDS by the direct-to-LDS load (64 lanes x 16
 // bytes land as one contiguous 1 KB block), so loads need no VGPRs and
-// STAGES-1 stages are in flight while the matrix cores work on the oldest one.
+// STAGES-1 stages are in flight while the matrix cores work on the oldest one
+// (the one-tile wide kernel: two A stages and three B stages, k_loop_roles).
 // The buffer form of that load (a descriptor per operand, 32-bit offsets) is
 // used whenever the rows fit a 4 GiB window: with the global form, a FLAT
 // instruction, in flight, the compiler drains every LDS read before each MFMA
@@ -73,13 +74,21 @@
 // adding the LDS fragment reads costs nothing.  With the operand streaming on
 // top, the chip's power management lowers the shader clock (about 2.2 GHz ->
 // 1.5-2.1 GHz) and a full 256 x 256 tile takes ~1.45x the cycles of its MFMAs.
-// Deeper pipelines (BK 32 with 4-5 stages, a third weight buffer),
-// register-staged loads, loads interleaved with the MFMAs, round-robin XCD
-// dealing of all m-tiles and 4-wave 128 x 128 wave tiles all measured no
-// faster.  What did help: a K loop whose body holds no branch, with the wave's
-// count of live 32-row blocks chosen once before the loop (5-12% on the larger
-// workloads); the size-balanced, interleaved tile order (xcd_tile); the staged
-// epilogue; the compact small-tile loop.
+// Per-K-step timestamps place the loss at the start of each step: a load
+// instruction holds its wave until the texture unit takes it, so while the
+// eight waves issued a 64 KB stage no MFMA ran for 800-1150 of ~3300 cycles.
+// The one-tile wide kernel therefore gives the two waves of a SIMD different
+// load roles (k_loop_roles, with a third weight buffer): 3280 -> 2875 cycles
+// per step, of which the power limit returns part as a lower clock (layer
+// 2-3% faster on packed16k and the Zipf workload, same bits).  Alone, a third
+// weight buffer, loads spread over the sub-steps, one wave row issuing every
+// load, BK 32 with 4-5 stages, a 256 x 128 tile with three stages,
+// register-staged loads, round-robin XCD dealing of all m-tiles and 4-wave
+// 128 x 128 wave tiles all measured no faster.  What did help besides: a K
+// loop whose body holds no branch, with the wave's count of live 32-row blocks
+// chosen once before the loop (5-12% on the larger workloads); the
+// size-balanced, interleaved tile order (xcd_tile); the staged epilogue; the
+// compact small-tile loop.
 #include <algorithm>
 #include <type_traits>
 
@@ -286,6 +295,23 @@ struct TileLoader {
       load_b<kNt>(t, koff, base + small_a<SROWS>() + (wave * LB + t) * 1024);
   }
 
+  // Rings of the one-tile wide kernel: two A stages, then three B stages.
+  static constexpr int A_BYTES = BM * G::ROW_BYTES, B_BYTES = BN * G::ROW_BYTES;
+  __device__ __forceinline__ void issue_a(char* smem, int kt, int abuf) const {
+    char* base = smem + abuf * A_BYTES;
+    const int koff = kt * G::ROW_BYTES;
+#pragma unroll
+    for (int t = 0; t < LA; ++t)
+      if (t < live_a) load_a(t, koff, base + (wave * LA + t) * 1024);
+  }
+  template <bool kNt>
+  __device__ __forceinline__ void issue_b(char* smem, int kt, int bbuf) const {
+    char* base = smem + 2 * A_BYTES + bbuf * B_BYTES;
+    const int koff = kt * G::ROW_BYTES;
+#pragma unroll
+    for (int t = 0; t < LB; ++t) load_b<kNt>(t, koff, base + (wave * LB + t) * 1024);
+  }
+
   // Loads one stage.  A blocks of 1 KB that lie wholly past the tile's rows are
   // not loaded (their LDS rows feed only outputs that are never stored), so a
   // wave issues live_a + LB loads per stage.
@@ -454,22 +480,99 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
   }
 }
 
+// The K loop of the one-tile wide kernel (256 x 256, two waves per SIMD).
+// Each load instruction holds its wave in issue until the CU's texture unit
+// takes it, at 16-20 cycles per 1 KB; with all eight waves issuing a 64 KB
+// stage at the start of a K step, no wave reached its MFMAs for the first
+// 800-1150 of about 3300 cycles.  So the two waves of a SIMD take different
+// roles.  The second (wave row 1) issues the next step's rows of A at the
+// start of the step; the first (wave row 0), which gets the matrix pipe first
+// and used to wait about 1000 cycles at the barrier, starts its MFMAs at once
+// and issues the weight rows of B two steps ahead once its MFMAs are issued.
+// A stays double-buffered and B triple-buffered (2 x 32 + 3 x 32 KB).  Loader
+// slot q = wave % 4 of a four-wave loader layout covers the same rows in
+// either role.
+template <int F, int FM, int FN, int WM, int WN, int BM, int BK, bool kNt, class Loader>
+__device__ __forceinline__ void k_loop_roles(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem,
+                                             int KT, int lane, int wm, int wn) {
+  using G = StageGeom<BK>;
+  constexpr int KS = BK / 16;
+  const bool a_role = wm != 0;
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  for (int kt = 0; kt < KT; ++kt) {
+    // an A wave's newest load is A(kt); a B wave may still have B(kt + 1)
+    // pending behind B(kt)
+    wait_loads(!a_role && kt + 1 < KT ? Loader::LB : 0);
+    __builtin_amdgcn_s_barrier();
+    const char* sa = smem + (kt & 1) * Loader::A_BYTES;
+    const char* sb = smem + 2 * Loader::A_BYTES + (kt % 3) * Loader::B_BYTES;
+    if constexpr (F > 0) {
+      bf16x8 af[2][F], bfr[2][FN];
+      auto frag = [&](int kk, int b) __attribute__((always_inline)) {
+        const int fo = G::frag_offset(lane, kk);
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+          af[b][i] = *(const bf16x8*)(sa + (wm * WM + i * 32) * G::ROW_BYTES + fo);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[b][j] = *(const bf16x8*)(sb + (wn * WN + j * 32) * G::ROW_BYTES + fo);
+      };
+      frag(0, 0);
+      if (a_role && kt + 1 < KT) ld.issue_a(smem, kt + 1, (kt + 1) & 1);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        if (kk + 1 < KS) frag(kk + 1, (kk + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (!a_role && kt + 2 < KT) ld.template issue_b<kNt>(smem, kt + 2, (kt + 2) % 3);
+    } else {
+      if (a_role && kt + 1 < KT) ld.issue_a(smem, kt + 1, (kt + 1) & 1);
+      if (!a_role && kt + 2 < KT) ld.template issue_b<kNt>(smem, kt + 2, (kt + 2) % 3);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  }
+}
+
 // K loop of a tile on the wide path: the first STAGES - 1 stages, then
 // k_loop over the 32-row blocks of this wave's band that hold rows of the
 // tile.  Blocks past them feed only outputs that are never stored, so a wide
 // tile skips their MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block
 // loop, 3 runs the full one).  A one-block band always runs its MFMAs: a
 // wave-uniform branch there measured slower than the wasted work.
-template <int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, bool kNt, class Loader>
+// (kRoles: the one-tile wide kernel's role split, k_loop_roles.)
+template <int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, bool kNt, bool kRoles,
+          class Loader>
 __device__ __forceinline__ void wide_k(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem, int KT,
                                        int per_stage, int lane, int wm, int wn, int rows) {
+  if constexpr (kRoles) {
+    if (wm != 0) {
+      ld.issue_a(smem, 0, 0);
+    } else {
+      ld.template issue_b<kNt>(smem, 0, 0);
+      if (1 < KT) ld.template issue_b<kNt>(smem, 1, 1);
+    }
+  } else {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < KT) ld.template issue<kNt>(smem, s, s);
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < KT) ld.template issue<kNt>(smem, s, s);
+  }
   const int band_rows = rows - wm * WM;
   const int fm_live = band_rows <= 0 ? 0 : (band_rows + 31) / 32;
-#define MOE_K_LOOP(F) \
-  k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn)
+#define MOE_K_LOOP(F)                                                                              \
+  do {                                                                                             \
+    if constexpr (kRoles)                                                                          \
+      k_loop_roles<F, FM, FN, WM, WN, BM, BK, kNt, Loader>(acc, ld, smem, KT, lane, wm, wn);       \
+    else                                                                                           \
+      k_loop<F, FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane,   \
+                                                             wm, wn);                              \
+  } while (0)
   if constexpr (FM == 1) {
     MOE_K_LOOP(1);
   } else {
@@ -549,19 +652,22 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   using Loader = TileLoader<kGateUp, BM, BN, NW, WN, BK, kBuf>;
+  // the one-tile wide kernel splits the loads by wave role (k_loop_roles)
+  constexpr bool kRoles = NW == 8 && !kLoop;
+  using RoleLoader = TileLoader<kGateUp, BM, BN, kRoles ? NW / 2 : NW, WN, BK, kBuf>;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(!kGateUp || WN % 64 == 0, "gate/up halves");
   static_assert(STAGES >= 2, "pipeline depth");
   static_assert((STAGES - 2) * (Loader::LA + Loader::LB) <= 24, "wait_loads range");
   constexpr int kSmemBytes =
-      cmax(STAGES * Loader::STAGE_BYTES,
+      cmax(kRoles ? 2 * Loader::A_BYTES + 3 * Loader::B_BYTES : STAGES * Loader::STAGE_BYTES,
            FM >= 4 ? cmax(3 * Loader::template small_stage<160>(),
                           cmax(3 * Loader::template small_stage<32>(),
                                3 * Loader::template small_stage<64>()))
                    : 0);
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   // Tiles of this workgroup: position q of its XCD's sequence, and with kLoop
   // also q + G, q + 2G, ... (G = the XCD's workgroups: the host then launches
@@ -579,9 +685,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
     int mt, nt;
     if (!xcd_tile_at(tm, a.n_tiles, xcd, q, (32 + a.n_tiles - 1) / a.n_tiles, &mt, &nt)) break;
     const TileRows tr = tm.locate(a.off0, a.off1, BM, mt);
-    Loader ld;
-    ld.init(a, tr, nt, lane, wave);
-    const int per_stage = ld.live_a + Loader::LB;  // loads this wave issues per stage
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -612,24 +715,33 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
       k_loop_small<F1, SR, 3, FM, FN, WN, BK, kNt, Loader>(acc, ld, smem, KT, per_stage, lane,   \
                                                            wn, F0 * 32);                         \
   } while (0)
-    bool compact = false;
-    if constexpr (kSmallPath) {
-      compact = true;
-      if (tr.rows <= 32)
-        MOE_K_SMALL(32);
-      else if (tr.rows <= 64)
-        MOE_K_SMALL(64);
-      else if (tr.rows <= 128)
-        MOE_K_SMALL(128);
-      else if (tr.rows <= 160)
-        MOE_K_SMALL(160);
-      else
-        compact = false;
+    if (kSmallPath && tr.rows <= 160) {
+      if constexpr (kSmallPath) {
+        Loader ld;
+        ld.init(a, tr, nt, lane, wave);
+        const int per_stage = ld.live_a + Loader::LB;  // loads this wave issues per stage
+        if (tr.rows <= 32)
+          MOE_K_SMALL(32);
+        else if (tr.rows <= 64)
+          MOE_K_SMALL(64);
+        else if (tr.rows <= 128)
+          MOE_K_SMALL(128);
+        else
+          MOE_K_SMALL(160);
+      }
+    } else if constexpr (kRoles) {
+      RoleLoader ld;
+      ld.init(a, tr, nt, lane, wave % (NW / 2));
+      wide_k<FM, FN, WM, WN, BM, BK, STAGES, kNt, true, RoleLoader>(acc, ld, smem, KT, 0, lane, wm,
+                                                                    wn, tr.rows);
+    } else {
+      Loader ld;
+      ld.init(a, tr, nt, lane, wave);
+      const int per_stage = ld.live_a + Loader::LB;
+      wide_k<FM, FN, WM, WN, BM, BK, STAGES, kNt, false, Loader>(acc, ld, smem, KT, per_stage, lane,
+                                                                 wm, wn, tr.rows);
     }
 #undef MOE_K_SMALL
-    if (!compact)
-      wide_k<FM, FN, WM, WN, BM, BK, STAGES, kNt, Loader>(acc, ld, smem, KT, per_stage, lane, wm, wn,
-                                                          tr.rows);
     };
     if (tr.single)
       run_k(std::true_type{});
