@@ -306,6 +306,29 @@ def test_compact_tile_row_classes_every_row(N):
     assert e <= TOL["bf16"], e
 
 
+@pytest.mark.parametrize("H,I", [(64, 128), (192, 64), (128, 192), (192, 256)])
+def test_wide_tile_few_k_steps_every_row(H, I):
+    """The 256 x 256 one-tile kernel with 1 to 4 K steps of 64 (its load roles
+    issue the first A stage and two B stages before the loop, then A one step
+    and B two steps ahead, so the shortest loops skip those issues and change
+    the final waits): gate/up K = H (1 or 3 steps on the wide tile; I = 64 and
+    192 run gate/up on the 64 x 128 tile), down K = I (1 to 4 steps), over 4096
+    rows of 8 experts (wide tiles with ragged tails).  Every row against the
+    oracle; N = 2 equals N = 1 bit for bit."""
+    cfg = C["bf16_e64_zipf"].with_(T=1024, E=8, k=4, H=H, I=I)
+    L = build_layer(cfg)
+    say(f"wide tile few K steps H={H} I={I}")
+    out, err = run_forward(L, L.shape(1))
+    assert err == 0
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, 1)
+    assert meta["n_invalid"] == 0 and meta["counts"].max() > 256
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL["bf16"], e
+    out2, _ = run_forward(L, L.shape(2))
+    assert torch.equal(out2, out)
+
+
 @pytest.mark.parametrize("name,kw", [
     ("odd_dims_bf16", dict(T=50, k=64, E=96, H=128, I=128, groups=2)),
     ("odd_dims_f32", dict(T=29, k=64, E=70, H=36, I=20, groups=1)),
