@@ -306,6 +306,43 @@ def test_compact_tile_row_classes_every_row(N):
     assert e <= TOL["bf16"], e
 
 
+def _random_forward_cases(n=12, seed=2024):
+    """Seeded random layer shapes: every third one has at least 4096 assignments
+    (the 256 x 256 instance with its load roles and compact tiles), the others
+    run the 64 x 128 instance; H and I multiples of 64, any E, k, T and N."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        big = i % 3 == 0
+        k = int(rng.integers(1, 9))
+        E = int(rng.integers(max(k, 2), 300))
+        T = int(rng.integers(4096 // k + 1, 4096 // k + 400)) if big else int(rng.integers(1, 700))
+        H = 64 * int(rng.integers(1, 9 if big else 17))
+        I = 64 * int(rng.integers(1, 7 if big else 9))
+        N = int(rng.integers(1, 6))
+        cases.append((T, H, E, k, I, N))
+    return cases
+
+
+@pytest.mark.parametrize("T,H,E,k,I,N", _random_forward_cases())
+def test_forward_random_shapes_every_row(T, H, E, k, I, N):
+    """Random shapes (Zipf-skewed routing, bf16): every row against the oracle,
+    and the chunked output equal to the unchunked one bit for bit."""
+    cfg = C["bf16_e64_zipf"].with_(T=T, E=E, k=k, H=H, I=I, seed=T + E, weight_seed=H + I)
+    L = build_layer(cfg)
+    say(f"random shape T={T} H={H} E={E} k={k} I={I} N={N}")
+    out, err = run_forward(L, L.shape(N))
+    assert err == 0
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, N)
+    assert meta["n_invalid"] == 0
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL["bf16"], e
+    if N > 1:
+        out1, _ = run_forward(L, L.shape(1))
+        assert torch.equal(out1, out)
+
+
 @pytest.mark.parametrize("H,I", [(64, 128), (192, 64), (128, 192), (192, 256)])
 def test_wide_tile_few_k_steps_every_row(H, I):
     """The 256 x 256 one-tile kernel with 1 to 4 K steps of 64 (its load roles
