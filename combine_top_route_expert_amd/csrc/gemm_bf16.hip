@@ -16,7 +16,7 @@
 // (weight) tiles is copied HBM -> LDS by the direct-to-LDS load (64 lanes x 16
 // bytes land as one contiguous 1 KB block), so loads need no VGPRs and
 // STAGES-1 stages are in flight while the matrix cores work on the oldest one
-// (the one-tile wide kernel: two A stages and three B stages, k_loop_roles).
+// (the wide 256 x 256 kernel: two A stages and three B stages, k_loop_roles).
 // The buffer form of that load (a descriptor per operand, 32-bit offsets) is
 // used whenever the rows fit a 4 GiB window: with the global form, a FLAT
 // instruction, in flight, the compiler drains every LDS read before each MFMA
@@ -77,10 +77,11 @@
 // Per-K-step timestamps place the loss at the start of each step: a load
 // instruction holds its wave until the texture unit takes it, so while the
 // eight waves issued a 64 KB stage no MFMA ran for 800-1150 of ~3300 cycles.
-// The one-tile wide kernel therefore gives the two waves of a SIMD different
+// The wide 256 x 256 kernel therefore gives the two waves of a SIMD different
 // load roles (k_loop_roles, with a third weight buffer): 3280 -> 2875 cycles
 // per step, of which the power limit returns part as a lower clock (layer
-// 2-3% faster on packed16k and the Zipf workload, same bits).  Alone, a third
+// 2-3% faster on packed16k, the Zipf workload and, in the tile-loop form, the
+// two-expert skew; same bits).  Alone, a third
 // weight buffer, loads spread over the sub-steps, one wave row issuing every
 // load, BK 32 with 4-5 stages, a 256 x 128 tile with three stages,
 // register-staged loads, round-robin XCD dealing of all m-tiles and 4-wave
@@ -295,7 +296,7 @@ struct TileLoader {
       load_b<kNt>(t, koff, base + small_a<SROWS>() + (wave * LB + t) * 1024);
   }
 
-  // Rings of the one-tile wide kernel: two A stages, then three B stages.
+  // Rings of the wide 256 x 256 kernel: two A stages, then three B stages.
   static constexpr int A_BYTES = BM * G::ROW_BYTES, B_BYTES = BN * G::ROW_BYTES;
   __device__ __forceinline__ void issue_a(char* smem, int kt, int abuf) const {
     char* base = smem + abuf * A_BYTES;
@@ -480,7 +481,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
   }
 }
 
-// The K loop of the one-tile wide kernel (256 x 256, two waves per SIMD).
+// The K loop of the wide 256 x 256 kernel (two waves per SIMD).
 // Each load instruction holds its wave in issue until the CU's texture unit
 // takes it, at 16-20 cycles per 1 KB; with all eight waves issuing a 64 KB
 // stage at the start of a K step, no wave reached its MFMAs for the first
@@ -546,7 +547,7 @@ __device__ __forceinline__ void k_loop_roles(f32x16 (&acc)[FM][FN], const Loader
 // tile skips their MFMAs (a band of 1 or 2 live blocks runs the 1- or 2-block
 // loop, 3 runs the full one).  A one-block band always runs its MFMAs: a
 // wave-uniform branch there measured slower than the wasted work.
-// (kRoles: the one-tile wide kernel's role split, k_loop_roles.)
+// (kRoles: the wide kernel's role split, k_loop_roles.)
 template <int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, bool kNt, bool kRoles,
           class Loader>
 __device__ __forceinline__ void wide_k(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem, int KT,
@@ -652,8 +653,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
   using Loader = TileLoader<kGateUp, BM, BN, NW, WN, BK, kBuf>;
-  // the one-tile wide kernel splits the loads by wave role (k_loop_roles)
-  constexpr bool kRoles = NW == 8 && !kLoop;
+  // the wide kernel splits the loads by wave role (k_loop_roles)
+  constexpr bool kRoles = NW == 8;
   using RoleLoader = TileLoader<kGateUp, BM, BN, kRoles ? NW / 2 : NW, WN, BK, kBuf>;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(!kGateUp || WN % 64 == 0, "gate/up halves");
@@ -667,7 +668,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
                    : 0);
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
 
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane0 = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   // Tiles of this workgroup: position q of its XCD's sequence, and with kLoop
   // also q + G, q + 2G, ... (G = the XCD's workgroups: the host then launches
@@ -676,6 +677,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) grouped_gemm_bf16(Gemm
   // thousands of workgroups that find none).
   const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
   for (int q = blockIdx.x >> 3;; q += wg_per_xcd) {
+    // In the tile loop the compiler hoisted every lane-derived address (loader
+    // offsets, fragment offsets) out of the loop and kept them all live: 256
+    // VGPRs and spills.  An opaque copy of the lane index per tile keeps them
+    // inside (238 VGPRs, no VGPR spills with the load roles).
+    int lane = lane0;
+    if constexpr (kLoop) asm volatile("" : "+v"(lane));
     // (built per tile: kept across the K loop it would cost registers)
     MTileMap tm;
     // the wide tile (one workgroup per CU) orders small experts' m-tiles by size

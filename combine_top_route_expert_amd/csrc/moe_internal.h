@@ -325,14 +325,16 @@ struct MTileMap {
         }
       }
     }
+    // the owner's values, broadcast to the wave, are wave-uniform: kept in
+    // scalar registers (as vector registers they stayed live across the K loop)
     TileRows r;
-    r.e = __shfl(fe, owner);
-    r.v0 = __shfl(fv0, owner);
-    r.rows = __shfl(frows, owner);
-    r.lo0 = __shfl(flo0, owner);
-    r.n0 = __shfl(fn0, owner);
-    r.lo1 = __shfl(flo1, owner);
-    r.single = __shfl(fsingle, owner);
+    r.e = __builtin_amdgcn_readfirstlane(__shfl(fe, owner));
+    r.v0 = __builtin_amdgcn_readfirstlane(__shfl(fv0, owner));
+    r.rows = __builtin_amdgcn_readfirstlane(__shfl(frows, owner));
+    r.lo0 = __builtin_amdgcn_readfirstlane(__shfl(flo0, owner));
+    r.n0 = __builtin_amdgcn_readfirstlane(__shfl(fn0, owner));
+    r.lo1 = __builtin_amdgcn_readfirstlane(__shfl(flo1, owner));
+    r.single = __builtin_amdgcn_readfirstlane(__shfl(fsingle, owner));
     return r;
   }
 };
