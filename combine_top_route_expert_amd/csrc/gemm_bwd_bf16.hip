@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) dgrad_gemm_bf16(DgradA
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   MTileMap tm;
   tm.build(a.off0, a.off1, a.E, BM, BM);
@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   int emt, nt;
   if (!xcd_tile_rr(a.E * a.m_tiles, a.n_tiles, &emt, &nt)) return;
