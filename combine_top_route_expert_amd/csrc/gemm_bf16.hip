@@ -553,6 +553,7 @@ template <int FM, int FN, int WM, int WN, int BM, int BK, int STAGES, bool kNt, 
 __device__ __forceinline__ void wide_k(f32x16 (&acc)[FM][FN], const Loader& ld, char* smem, int KT,
                                        int per_stage, int lane, int wm, int wn, int rows) {
   if constexpr (kRoles) {
+    // KT >= 1: H and I are positive multiples of 64 (checked at the boundary)
     if (wm != 0) {
       ld.issue_a(smem, 0, 0);
     } else {
