@@ -366,6 +366,26 @@ def test_wide_tile_few_k_steps_every_row(H, I):
     assert torch.equal(out2, out)
 
 
+@pytest.mark.parametrize("I", [64, 128])
+def test_tile_loop_few_k_steps_every_row(I):
+    """The tile-loop form of the 256 x 256 kernel (4096 rows over E = 256, so the
+    grid is capped and workgroups take several tiles) with its load roles at one
+    and two K steps: the down GEMM with K = I = 64 and 128 over H = 2048 (eight
+    n-tiles).  Every row against the oracle; N = 2 equals N = 1 bit for bit."""
+    cfg = C["bf16_e64_zipf"].with_(T=1024, E=256, k=4, H=2048, I=I)
+    L = build_layer(cfg)
+    say(f"tile loop few K steps I={I}")
+    out, err = run_forward(L, L.shape(1))
+    assert err == 0
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, 1)
+    assert meta["n_invalid"] == 0
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL["bf16"], e
+    out2, _ = run_forward(L, L.shape(2))
+    assert torch.equal(out2, out)
+
+
 @pytest.mark.parametrize("name,kw", [
     ("odd_dims_bf16", dict(T=50, k=64, E=96, H=128, I=128, groups=2)),
     ("odd_dims_f32", dict(T=29, k=64, E=70, H=36, I=20, groups=1)),
