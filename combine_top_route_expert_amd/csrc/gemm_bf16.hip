@@ -349,17 +349,19 @@ __device__ __forceinline__ void wait_loads(int n) {
 #undef MOE_WAIT_CASE
 }
 
-// Epilogue through LDS.  MFMA 32x32 output: lane l holds column l % 32 of
-// rows 8*(q/4) + 4*(l/32) + q%4, q = 0..15, of each block.  Every wave writes
-// its nblk 32-row blocks from row row0 (after SwiGLU for gate_up) as bf16 into a
-// row-major C tile in the freed stage buffers, then the workgroup stores the
-// tile 16 bytes per lane, one row segment at a time.  (Storing each lane's
-// 2-byte elements straight from the MFMA layout took one guarded global store
-// per element.)  Chunk ch (8 elements) of tile row r sits at chunk
-// ch ^ 4((r/4) mod 2), so that the two rows a 2-byte LDS write covers (r and
-// r + 4) fall in different banks.  Same values, same bits.  PLANES = 3
-// (gate_up in the backward's recompute) also saves g and u into the joint
-// [rows][2I] copy: one plane per pass.
+// Epilogue through LDS.  The K loops pass the weight fragment as the MFMA's
+// first operand and the row fragment as its second, so each 32x32 block holds
+// C transposed: lane l holds row l % 32 of columns 8*(q/4) + 4*(l/32) + q%4,
+// q = 0..15 (the products and their order over K are those of the other
+// operand order: same bits).  A lane's four consecutive columns of a row go to
+// LDS as one 8-byte write (with the rows in each lane's columns, one 2-byte
+// write per element had taken four times the LDS writes and twice the
+// conversions: down GEMM 2-2.5% slower).  Every wave writes its nblk 32-row
+// blocks from row row0 (after SwiGLU for gate_up) as bf16 into a row-major C
+// tile in the freed stage buffers, then the workgroup stores the tile 16 bytes
+// per lane, one row segment at a time.  PLANES = 3 (gate_up in the backward's
+// recompute) also saves g and u into the joint [rows][2I] copy: one plane per
+// pass.
 template <bool kGateUp, int PLANES, int FM, int FN, int BM, int BN, int WM, int WN, int NT>
 __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[FM][FN],
                                                const TileRows& tr, int nt, int row0, int nblk,
@@ -368,10 +370,14 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
   constexpr int CPR = CT / 8;                // 16-byte chunks per tile row
   static_assert(CPR >= 8, "chunk swizzle needs 8 chunks per row");
   static_assert(PLANES == 1 || kGateUp, "g and u exist for gate_up only");
+  // chunk ch of row r at slot ch ^ (r mod CPR): the 32 rows of one 8-byte
+  // write (a row per lane, lanes l and l + 32 the two halves of one chunk)
+  // fall in distinct slots
   auto lds_at = [](int r, int c) {
-    return r * (CT * 2) + ((((c >> 3) ^ (((r >> 2) & 1) << 2))) << 4) + (c & 7) * 2;
+    return r * (CT * 2) + (((c >> 3) ^ (r & (CPR - 1))) << 4) + (c & 7) * 2;
   };
-  const int rbase = row0 + 4 * (lane >> 5);
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const int rl = row0 + (lane & 31), cq = 4 * (lane >> 5);
   const int col0 = nt * CT;
   const uint16_t* const cbase[2] = {a.C[0], a.C[1]};
 #pragma unroll
@@ -381,22 +387,30 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
     for (int i = 0; i < FM; ++i) {
       // blocks past the wave's band or the tile's rows: never stored
       if (i >= nblk || row0 + i * 32 >= tr.rows) break;
+      const int r = rl + i * 32;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+      for (int g4 = 0; g4 < 4; ++g4) {
         if constexpr (kGateUp) {
 #pragma unroll
           for (int j = 0; j < FN / 2; ++j) {
-            const int c = wn * (WN / 2) + j * 32 + (lane & 31);
-            const float g = acc[i][j][q], u = acc[i][j + FN / 2][q];
-            const float v = plane == 0 ? swiglu(g, u) : plane == 1 ? g : u;
-            *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(v);
+            const int c = wn * (WN / 2) + j * 32 + 8 * g4 + cq;
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float g = acc[i][j][4 * g4 + t], u = acc[i][j + FN / 2][4 * g4 + t];
+              v[t] = plane == 0 ? swiglu(g, u) : plane == 1 ? g : u;
+            }
+            *(bf16x4*)(smem + lds_at(r, c)) =
+                bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
           }
         } else {
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const int c = wn * WN + j * 32 + (lane & 31);
-            *(uint16_t*)(smem + lds_at(r, c)) = to_bf16_bits(acc[i][j][q]);
+            const int c = wn * WN + j * 32 + 8 * g4 + cq;
+            const f32x16& x = acc[i][j];
+            *(bf16x4*)(smem + lds_at(r, c)) =
+                bf16x4{(__bf16)x[4 * g4], (__bf16)x[4 * g4 + 1], (__bf16)x[4 * g4 + 2],
+                       (__bf16)x[4 * g4 + 3]};
           }
         }
       }
@@ -468,7 +482,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[FM][FN], const Loader& ld, 
         for (int i = 0; i < F; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j],
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i],
                                                                 acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -528,7 +542,7 @@ __device__ __forceinline__ void k_loop_roles(f32x16 (&acc)[FM][FN], const Loader
         for (int i = 0; i < F; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j],
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk & 1][j], af[kk & 1][i],
                                                                 acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -614,7 +628,7 @@ __device__ __forceinline__ void compact_mfma(f32x16 (&acc)[FM][FN], const char* 
       for (int i = 0; i < F; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
   }
 }
