@@ -501,7 +501,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   };
@@ -516,7 +516,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
   constexpr int CPR = BN / 4;  // 16-byte chunks per row
   float* Ce = a.C + (int64_t)e * a.M * a.N;
   float* cl = (float*)smem;
-  const int rl = 4 * (lane >> 5);  // row of q = 0 within a 32-row block
+  // the MFMAs above take the B fragment first, so each block holds C
+  // transposed: lane l has row l % 32 and columns 8(q/4) + 4(l/32) + q%4, four
+  // consecutive columns per group of q, written as one 16-byte LDS store.
+  // 16-byte chunk ch of row r at slot ch ^ (r mod 32): the 32 rows of one
+  // store fall in distinct slots.
+  auto cl_at = [](int r, int c) { return r * BN + ((((c >> 2) ^ (r & 31))) << 2); };
+  const int rq = lane & 31, cq = 4 * (lane >> 5);
 #pragma unroll
   for (int h = 0; h < WAVES_M; ++h) {
     __syncthreads();  // the stage buffers (or the previous pass) are free
@@ -524,18 +530,20 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N) wgrad_gemm_bf16(WgradA
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = rl + i * 32 + 8 * (q >> 2) + (q & 3);
+        for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) cl[r * BN + wn * WN + j * 32 + (lane & 31)] = acc[i][j][q];
-        }
+          for (int j = 0; j < FN; ++j) {
+            const f32x16& x = acc[i][j];
+            *(float4*)(cl + cl_at(i * 32 + rq, wn * WN + j * 32 + 8 * g4 + cq)) =
+                make_float4(x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]);
+          }
     }
     __syncthreads();
     for (int ch = threadIdx.x; ch < WM * CPR; ch += blockDim.x) {
       const int r = ch / CPR, c = (ch % CPR) * 4;
       const int m = mt * BM + h * WM + r, n = nt * BN + c;
       if (m >= a.M || n >= a.N) continue;
-      float4 v = *(const float4*)(cl + r * BN + c);
+      float4 v = *(const float4*)(cl + cl_at(r, c));
       float4* dst = (float4*)(Ce + (int64_t)m * a.N + n);
       if (a.accumulate) {
         const float4 old = *dst;
