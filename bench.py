@@ -72,14 +72,32 @@ def make_inputs(cfg, torch, synth):
             "idx_np": idx, "w_np": w, "counts": np.bincount(idx.ravel(), minlength=cfg.E)}
 
 
+_STREAM_PAIR = []
+
+
+def stream_pair(torch):
+    """The two streams of the two-stream schedules: the first two streams the
+    process takes from torch's stream pool, created once and reused.  HIP runs
+    its streams on a few hardware queues (four by default); the null stream holds
+    the first, the next streams created each get one of their own, and later ones
+    share them.  Two streams on one queue run their kernels one after another, so
+    a pair taken later could serialise the schedule (a kernel trace showed an
+    arbitrary pool stream on the null stream's queue)."""
+    if not _STREAM_PAIR:
+        _STREAM_PAIR.extend((torch.cuda.Stream(), torch.cuda.Stream()))
+    return _STREAM_PAIR[0], _STREAM_PAIR[1]
+
+
 def time_layer(moe, torch, shape, inp, steps, warmup, two_streams=True,
                schedule=None):
     cfg_dtype = shape.torch_dtype
     out = torch.empty((shape.T, shape.H), dtype=cfg_dtype, device="cuda")
     ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    s0 = torch.cuda.current_stream()
-    s1 = torch.cuda.Stream() if two_streams else None
+    if two_streams:
+        s0, s1 = stream_pair(torch)
+    else:
+        s0, s1 = torch.cuda.current_stream(), None
 
     def step():
         if schedule is None:
@@ -481,6 +499,7 @@ def main():
 
     moe.load_library()
     torch.cuda.set_device(0)
+    stream_pair(torch)  # before any other stream, so that each gets a hardware queue
     cfg = synth.CONFIGS[args.config]
     N = args.num_chunks
     log(f"inputs {cfg.name}")

@@ -296,6 +296,10 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  *    streams, as the Ascend dual-stream article's "01 Prefill micro-batch雙流並行"
  *    splits the work, here by experts, so that no weight is read twice).  Same
  *    bits; without a distinct s1 it is the pair-fused schedule.
+ * The overlap also needs s0 and s1 on different hardware queues: HIP runs its
+ * streams on a few of them (GPU_MAX_HW_QUEUES, four by default), given out as
+ * streams are created, and two streams that share a queue run their launches
+ * one after another (same bits, no overlap).
  * s1 == s0 (or null) is legal and gives the same bits without overlap; the
  * result never depends on N or on the schedule.  On return s0 is ordered after
  * all work of the call.  ws must hold moe_workspace_size bytes.  dev_error is
