@@ -23,7 +23,7 @@ Sources (page title, then the section each function follows):
 * [CANN-blog] MoE communication blog, section 4.2 (mixed precision): router
   probabilities stay fp32.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * expert FFN = SwiGLU without bias: FFN_e(x) = W_d[e] (silu(W_g[e] x) * (W_u[e] x)),
   silu(z) = z / (1 + e^-z); ``w_gate_up[e]`` is [2I, H] (gate rows first),
