@@ -68,7 +68,7 @@ extern "C" {
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,          /* null/misaligned pointer, bad size, chunk out of range */
-  MOE_ERR_UNSUPPORTED = 2,          /* valid but outside this build's shape limits */
+  MOE_ERR_UNSUPPORTED = 2,          /* valid but outside the library's shape limits */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below what the *_workspace_size call returns */
   MOE_ERR_HIP = 4                   /* a HIP runtime call or kernel launch failed */
 } moe_status;
