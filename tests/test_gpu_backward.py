@@ -190,6 +190,50 @@ def test_backward_chunk_invariance(name, Ns):
                 assert rel <= 1e-5, (N, two, rel)
 
 
+def _random_backward_cases(n=8, seed=4242):
+    """Seeded random layer shapes for the backward: bf16 with H and I multiples
+    of 64 (every third with at least 4096 assignments, the 256 x 256 instance of
+    the recomputed forward), and two fp32 ones with H and I multiples of 4; any
+    k, T and N; E at most 64 so the oracle's float64 weight gradients stay small."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        f32 = i >= n - 2
+        big = not f32 and i % 3 == 0
+        k = int(rng.integers(1, 9))
+        E = int(rng.integers(max(k, 2), 65))
+        T = int(rng.integers(4096 // k + 1, 4096 // k + 300)) if big else int(rng.integers(1, 600))
+        step = 4 if f32 else 64
+        H = step * int(rng.integers(1, (256 if f32 else 512) // step + 1))
+        I = step * int(rng.integers(1, (192 if f32 else 384) // step + 1))
+        N = int(rng.integers(1, 6))
+        cases.append(("odd_dims_f32" if f32 else "bf16_e64_zipf", T, H, E, k, I, N))
+    return cases
+
+
+@pytest.mark.parametrize("name,T,H,E,k,I,N", _random_backward_cases())
+def test_backward_random_shapes_every_output(name, T, H, E, k, I, N):
+    """Random shapes (Zipf-skewed routing for bf16): every output of the backward
+    against the oracle, and grad_hidden and grad_w at N chunks equal to N = 1 bit
+    for bit."""
+    cfg = C[name].with_(T=T, E=E, k=k, H=H, I=I, groups=1, seed=T + E, weight_seed=H + I)
+    L = build_layer(cfg)
+    go = grad_out_for(L)
+    gh, gw, gwgu, gwd, err = run_backward(L, N, go)
+    ref = oracle.moe_backward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I, f64(go),
+                              cfg.groups, N)
+    tol = TOL[cfg.dtype]
+    assert err == ref["meta"]["n_invalid"] == 0
+    e_h = oracle.row_rel_err(f64(gh), ref["grad_hidden"])
+    e_w = norm_rel_err(f64(gw), ref["grad_w"])
+    say(f"  grad_hidden {e_h:.2e}  grad_w {e_w:.2e}")
+    assert e_h <= tol and e_w <= tol, (e_h, e_w)
+    check_weight_grads(L, ref, gwgu, gwd, tol)
+    if N > 1:
+        gh1, gw1, _, _, _ = run_backward(L, 1, go, two_streams=False)
+        assert torch.equal(gh1, gh) and torch.equal(gw1, gw)
+
+
 def test_backward_steps_vs_oracle_pieces():
     """moe_unpermute_combine_backward and moe_permute_backward on their own."""
     L = layer_for("bf16_e64_zipf", 512)
