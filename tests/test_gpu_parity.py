@@ -343,6 +343,42 @@ def test_forward_random_shapes_every_row(T, H, E, k, I, N):
         assert torch.equal(out1, out)
 
 
+def _random_forward_cases_f32(n=6, seed=2025):
+    """Seeded random fp32 layer shapes: H and I multiples of 4 (the fp32 path's
+    only alignment), any E, k, T and N."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        k = int(rng.integers(1, 9))
+        E = int(rng.integers(max(k, 2), 200))
+        T = int(rng.integers(1, 1500))
+        H = 4 * int(rng.integers(1, 129))
+        I = 4 * int(rng.integers(1, 97))
+        N = int(rng.integers(1, 6))
+        cases.append((T, H, E, k, I, N))
+    return cases
+
+
+@pytest.mark.parametrize("T,H,E,k,I,N", _random_forward_cases_f32())
+def test_forward_random_shapes_f32_every_row(T, H, E, k, I, N):
+    """Random fp32 shapes: every row against the oracle (fp32 tolerance), and the
+    chunked output equal to the unchunked one bit for bit."""
+    cfg = C["odd_dims_f32"].with_(T=T, E=E, k=k, H=H, I=I, groups=1, seed=T + E,
+                                  weight_seed=H + I)
+    L = build_layer(cfg)
+    say(f"random fp32 shape T={T} H={H} E={E} k={k} I={I} N={N}")
+    out, err = run_forward(L, L.shape(N))
+    assert err == 0
+    ref, meta = oracle.moe_forward(L.hidden64(), L.idx_np, L.w_np, L.expert64, cfg.E, cfg.I,
+                                   cfg.groups, N)
+    assert meta["n_invalid"] == 0
+    e = oracle.row_rel_err(f64(out), ref)
+    assert e <= TOL["f32"], e
+    if N > 1:
+        out1, _ = run_forward(L, L.shape(1))
+        assert torch.equal(out1, out)
+
+
 @pytest.mark.parametrize("H,I", [(64, 128), (192, 64), (128, 192), (192, 256)])
 def test_wide_tile_few_k_steps_every_row(H, I):
     """The 256 x 256 one-tile kernel with 1 to 4 K steps of 64 (its load roles
