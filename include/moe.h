@@ -300,6 +300,11 @@ moe_status moe_unpermute_combine(const moe_shape* shape, int32_t chunk, const vo
  * streams on a few of them (GPU_MAX_HW_QUEUES, four by default), given out as
  * streams are created, and two streams that share a queue run their launches
  * one after another (same bits, no overlap).
+ * Every schedule enqueues only kernels and event record / wait pairs (no
+ * memsets, allocations or host reads), and s1 is forked from s0 and joined
+ * back within the call, so a call can be captured in a HIP graph on s0 (the
+ * library's events are created on a thread's first call on a device: make
+ * that call before capturing).
  * s1 == s0 (or null) is legal and gives the same bits without overlap; the
  * result never depends on N or on the schedule.  On return s0 is ordered after
  * all work of the call.  ws must hold moe_workspace_size bytes.  dev_error is

@@ -782,3 +782,37 @@ def test_forward_and_backward_in_hip_graph():
             assert torch.equal(got, want), rep
         # eager work between replays
         run_forward(L, shape)
+
+
+@pytest.mark.parametrize("schedule", [moe.MOE_SCHEDULE_PER_CHUNK, moe.MOE_SCHEDULE_EXPERT_HALVES])
+def test_two_stream_schedules_in_hip_graph(schedule):
+    """The two-stream schedules order s1 after s0 and s0 after s1 with event
+    record / wait pairs only (no memsets or host reads), so a capture on s0
+    takes s1's work in and joins it back: every replay, with eager work and
+    synchronisations between replays, gives the eager bits."""
+    L = layer_for("bf16_e64_zipf", 1024)
+    shape = L.shape(4)
+    eager, _ = run_forward(L, L.shape(1))
+    out = torch.zeros_like(eager)
+    ws = torch.empty(moe.moe_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    s, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):  # warm-up on the capture stream (creates the library's events)
+        moe.moe_chunked_forward_schedule(shape, L.hidden, L.idx, L.w, L.wgu, L.wd, out, ws,
+                                         s0=s, s1=s1, schedule=schedule)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+    g = torch.cuda.CUDAGraph()
+    say(f"capture schedule {schedule}")
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_chunked_forward_schedule(shape, L.hidden, L.idx, L.w, L.wgu, L.wd, out, ws,
+                                         s0=torch.cuda.current_stream(), s1=s1,
+                                         schedule=schedule)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        run_forward(L, shape)  # eager work between replays
