@@ -784,7 +784,8 @@ def test_forward_and_backward_in_hip_graph():
         run_forward(L, shape)
 
 
-@pytest.mark.parametrize("schedule", [moe.MOE_SCHEDULE_PER_CHUNK, moe.MOE_SCHEDULE_EXPERT_HALVES])
+@pytest.mark.parametrize("schedule", [moe.MOE_SCHEDULE_PER_CHUNK, moe.MOE_SCHEDULE_EXPERT_HALVES,
+                                      moe.MOE_SCHEDULE_PAIR_FUSED_PREFETCH])
 def test_two_stream_schedules_in_hip_graph(schedule):
     """The two-stream schedules order s1 after s0 and s0 after s1 with event
     record / wait pairs only (no memsets or host reads), so a capture on s0
